@@ -1,0 +1,163 @@
+"""Python binding of libq8attn.so: exact chunked causal attention prefill over a Q8_0 KV cache
+on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP kernels behind the C
+ABI declared in ``include/q8attn.h``; PyTorch supplies device memory and streams.  The names and
+arguments mirror the C functions; tensors are accepted wherever the C function takes a pointer
+(raw integer addresses are accepted too).  If the shared library is not built, importing works
+but every call raises: there is no CPU fallback.
+
+The method ("Out-of-Core Flash Streaming & Speculative Decode (1M Context)", Sec. 3): the KV
+sequence is consumed in chunks while the online-softmax state (m, l, unnormalised O) of every
+query row persists across the calls, so O / l after the last chunk equals single-pass softmax
+attention.  Q8_0 is block_q8_0 of "Core Architecture & The 4-Brick Pipeline", Sec. 5.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8attn.so")
+
+Q8A_OK = 0
+Q8A_E_INVAL = 1
+Q8A_E_UNSUPPORTED = 2
+Q8A_E_ALIGN = 3
+Q8A_E_STATE = 4
+Q8A_E_HIP = 5
+KV_Q8_0 = 0
+KV_F16 = 1
+STATE_MAGIC = 0x51384154
+HEAD_DIM = 64
+ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
+
+EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_finalize",
+           "attn_accumulate_stream", "q8a_status_string", "q8a_last_hip_error")
+
+
+class Q8AError(RuntimeError):
+    def __init__(self, status: int, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = "%s (status %d)" % (status_string(status), status)
+        if status == Q8A_E_HIP:
+            msg += ", hipError_t %d" % hip_error
+        super().__init__(msg)
+
+
+class q8a_state(ctypes.Structure):
+    """Mirror of the C descriptor q8a_state."""
+    _fields_ = [("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("n_seq", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_q", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_pos0", ctypes.c_int64), ("magic", ctypes.c_uint32),
+                ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libq8attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libq8attn.so is not built (run __graft_entry__.build()); "
+                           "there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    SP = ctypes.POINTER(q8a_state)
+    lib.q8_0_pack.argtypes = [P, P, i64, i32, P]
+    lib.attn_state_init.argtypes = [SP, P, P, P, i32, i32, i32, i32, i64, P]
+    lib.attn_accumulate_chunk.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P]
+    lib.attn_finalize.argtypes = [SP, P, P, P]
+    lib.attn_accumulate_stream.argtypes = [SP, P, P, P, i32, i64, i32, ctypes.POINTER(P),
+                                           ctypes.POINTER(P), i32, P, P]
+    lib.q8a_status_string.restype = ctypes.c_char_p
+    lib.q8a_status_string.argtypes = [ctypes.c_int]
+    lib.q8a_last_hip_error.restype = ctypes.c_int
+    lib.q8a_last_hip_error.argtypes = []
+    for name in ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_finalize",
+                 "attn_accumulate_stream"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().q8a_status_string(int(status)).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != Q8A_OK:
+        raise Q8AError(rc, library().q8a_last_hip_error() if rc == Q8A_E_HIP else 0)
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def q8_0_pack(x, dst, n_rows: int, row_len: int, stream=None) -> None:
+    """FP32 [n_rows][row_len] -> Q8_0 bytes (n_rows * row_len/32 * 34), on the GPU."""
+    _check(library().q8_0_pack(_ptr(x), _ptr(dst), int(n_rows), int(row_len), _stream(stream)))
+
+
+def attn_state_init(m, l, o, n_seq: int, n_heads: int, n_q: int, head_dim: int, q_pos0: int,
+                    stream=None) -> q8a_state:
+    """Describe the state buffers and mark every row empty (m = -inf, l = 0)."""
+    st = q8a_state()
+    _check(library().attn_state_init(ctypes.byref(st), _ptr(m), _ptr(l), _ptr(o), int(n_seq),
+                                     int(n_heads), int(n_q), int(head_dim), int(q_pos0),
+                                     _stream(stream)))
+    return st
+
+
+def attn_accumulate_chunk(st: q8a_state, q, k, v, kv_dtype: int, kv_pos0: int, n_kv: int,
+                          kv_head_stride: int, kv_seq_stride: int, causal: int = 1,
+                          stream=None) -> None:
+    """Fold one KV chunk (keys at positions kv_pos0 .. kv_pos0 + n_kv - 1) into the state."""
+    _check(library().attn_accumulate_chunk(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v),
+                                           int(kv_dtype), int(kv_pos0), int(n_kv),
+                                           int(kv_head_stride), int(kv_seq_stride),
+                                           int(causal), _stream(stream)))
+
+
+def attn_finalize(st: q8a_state, out, lse=None, stream=None) -> None:
+    """out = O / l (FP16), lse = m + ln l (FP32)."""
+    _check(library().attn_finalize(ctypes.byref(st), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def attn_accumulate_stream(st: q8a_state, q, k_host, v_host, kv_dtype: int, n_kv_total: int,
+                           chunk_tokens: int, slot_k, slot_v, causal: int = 1,
+                           compute_stream=None, copy_stream=None) -> None:
+    """Stream a chunk-major pinned host KV cache through two device slots per tensor."""
+    sk = (ctypes.c_void_p * 2)(_ptr(slot_k[0]), _ptr(slot_k[1]))
+    sv = (ctypes.c_void_p * 2)(_ptr(slot_v[0]), _ptr(slot_v[1]))
+    _check(library().attn_accumulate_stream(ctypes.byref(st), _ptr(q), _ptr(k_host),
+                                            _ptr(v_host), int(kv_dtype), int(n_kv_total),
+                                            int(chunk_tokens), sk, sv, int(causal),
+                                            _stream(compute_stream), _stream(copy_stream)))
+
+
+def alloc_state(n_seq: int, n_heads: int, n_q: int, device="cuda"):
+    """Convenience: FP32 tensors m, l [n_seq,n_heads,n_q] and o [...,64] for a state."""
+    m = torch.empty((n_seq, n_heads, n_q), dtype=torch.float32, device=device)
+    l = torch.empty_like(m)
+    o = torch.empty((n_seq, n_heads, n_q, HEAD_DIM), dtype=torch.float32, device=device)
+    return m, l, o

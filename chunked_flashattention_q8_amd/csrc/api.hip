@@ -1,0 +1,271 @@
+// C ABI of libq8attn.so: argument validation, launch configuration and the double-buffered
+// host-to-device streaming loop.  Every check runs before anything is enqueued; on failure the
+// state descriptor is left as it was.
+#include <stdint.h>
+
+#include "q8attn.h"
+#include "q8attn_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_failure(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return Q8A_E_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int row_bytes(int32_t kv_dtype)
+{
+    return kv_dtype == Q8A_KV_Q8_0 ? q8a::kQ8RowBytes
+                                   : (kv_dtype == Q8A_KV_F16 ? q8a::kF16RowBytes : 0);
+}
+
+int check_state(const q8a_state *st)
+{
+    if (!st || st->magic != Q8A_STATE_MAGIC)
+        return Q8A_E_STATE;
+    if (st->head_dim != q8a::kHeadDim || st->n_seq < 1 || st->n_heads < 1 || st->n_q < 1 ||
+        !st->m || !st->l || !st->o || st->q_pos0 < 0)
+        return Q8A_E_STATE;
+    return Q8A_OK;
+}
+
+int64_t state_rows(const q8a_state *st)
+{
+    return (int64_t)st->n_seq * st->n_heads * st->n_q;
+}
+
+// Validation shared by the resident and the streamed accumulate paths.
+int check_chunk(const q8a_state *st, const void *q, const void *k, const void *v,
+                int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv, int64_t head_stride,
+                int64_t seq_stride, int32_t causal)
+{
+    int rc = check_state(st);
+    if (rc)
+        return rc;
+    const int row = row_bytes(kv_dtype);
+    if (!row)
+        return Q8A_E_INVAL;
+    if (!q || !k || !v || n_kv < 1 || kv_pos0 < 0 || (causal != 0 && causal != 1))
+        return Q8A_E_INVAL;
+    if ((int64_t)n_kv * row > INT32_MAX - 16) // per-head byte range is addressed with 32 bits
+        return Q8A_E_INVAL;
+    if (kv_pos0 > INT64_MAX / 2 || st->q_pos0 > INT64_MAX / 2)
+        return Q8A_E_INVAL;
+    if (head_stride < 0 || seq_stride < 0)
+        return Q8A_E_INVAL;
+    if (st->n_heads > 1 && head_stride < (int64_t)n_kv * row)
+        return Q8A_E_INVAL;
+    if (st->n_seq > 1 && seq_stride < (int64_t)n_kv * row)
+        return Q8A_E_INVAL;
+    if (st->n_heads > 65535 || st->n_seq > 65535)
+        return Q8A_E_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || head_stride % 16 ||
+        seq_stride % 16)
+        return Q8A_E_ALIGN;
+    return Q8A_OK;
+}
+
+q8a::AccumulateArgs make_args(const q8a_state *st, const void *q, const void *k, const void *v,
+                              int64_t kv_pos0, int32_t n_kv, int64_t head_stride,
+                              int64_t seq_stride, int32_t causal)
+{
+    q8a::AccumulateArgs a;
+    a.q = q;
+    a.k = static_cast<const uint8_t *>(k);
+    a.v = static_cast<const uint8_t *>(v);
+    a.m = st->m;
+    a.l = st->l;
+    a.o = st->o;
+    a.kv_head_stride = head_stride;
+    a.kv_seq_stride = seq_stride;
+    a.q_pos0 = st->q_pos0;
+    a.kv_pos0 = kv_pos0;
+    a.B = st->n_seq;
+    a.H = st->n_heads;
+    a.M = st->n_q;
+    a.n_kv = n_kv;
+    a.causal = causal;
+    return a;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *q8a_status_string(int status)
+{
+    switch (status) {
+    case Q8A_OK: return "ok";
+    case Q8A_E_INVAL: return "invalid argument";
+    case Q8A_E_UNSUPPORTED: return "unsupported configuration";
+    case Q8A_E_ALIGN: return "misaligned pointer or stride";
+    case Q8A_E_STATE: return "state descriptor not initialised or inconsistent";
+    case Q8A_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int q8a_last_hip_error(void) { return g_last_hip_error; }
+
+int q8_0_pack(const float *x, void *dst, int64_t n_rows, int32_t row_len, void *stream)
+{
+    if (n_rows < 0 || row_len <= 0 || row_len % 32)
+        return Q8A_E_INVAL;
+    if (n_rows == 0)
+        return Q8A_OK;
+    if (!x || !dst)
+        return Q8A_E_INVAL;
+    if (n_rows > ((int64_t)1 << 36) / (row_len / 32)) // grid and index ranges
+        return Q8A_E_INVAL;
+    if (!aligned(x, 16) || !aligned(dst, 2))
+        return Q8A_E_ALIGN;
+    const int64_t n_blocks = n_rows * (row_len / 32);
+    hipError_t e = q8a::launch_q8_0_pack(x, static_cast<uint8_t *>(dst), n_blocks,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
+int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
+                    int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0,
+                    void *stream)
+{
+    if (!st || !m || !l || !o || n_seq < 1 || n_heads < 1 || n_q < 1 || q_pos0 < 0)
+        return Q8A_E_INVAL;
+    if (head_dim != q8a::kHeadDim)
+        return Q8A_E_UNSUPPORTED;
+    if (n_heads > 65535 || n_seq > 65535 || (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 36))
+        return Q8A_E_UNSUPPORTED;
+    if (!aligned(m, 4) || !aligned(l, 4) || !aligned(o, 16))
+        return Q8A_E_ALIGN;
+    const int64_t rows = (int64_t)n_seq * n_heads * n_q;
+    hipError_t e = q8a::launch_state_init(m, l, rows, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_failure(e);
+    st->m = m;
+    st->l = l;
+    st->o = o;
+    st->n_seq = n_seq;
+    st->n_heads = n_heads;
+    st->n_q = n_q;
+    st->head_dim = head_dim;
+    st->q_pos0 = q_pos0;
+    st->magic = Q8A_STATE_MAGIC;
+    st->flags = 0;
+    return Q8A_OK;
+}
+
+int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, const void *v,
+                          int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
+                          int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
+                          void *stream)
+{
+    int rc = check_chunk(st, q, k, v, kv_dtype, kv_pos0, n_kv, kv_head_stride, kv_seq_stride,
+                         causal);
+    if (rc)
+        return rc;
+    q8a::AccumulateArgs a =
+        make_args(st, q, k, v, kv_pos0, n_kv, kv_head_stride, kv_seq_stride, causal);
+    hipError_t e = q8a::launch_accumulate(a, kv_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
+int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream)
+{
+    int rc = check_state(st);
+    if (rc)
+        return rc;
+    if (!out)
+        return Q8A_E_INVAL;
+    if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return Q8A_E_ALIGN;
+    hipError_t e = q8a::launch_finalize(st->m, st->l, st->o, out, lse, state_rows(st),
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
+int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_host,
+                           const void *v_host, int32_t kv_dtype, int64_t n_kv_total,
+                           int32_t chunk_tokens, void *const slot_k[2], void *const slot_v[2],
+                           int32_t causal, void *compute_stream, void *copy_stream)
+{
+    if (!slot_k || !slot_v || !k_host || !v_host || n_kv_total < 1 || chunk_tokens < 1)
+        return Q8A_E_INVAL;
+    for (int s = 0; s < 2; ++s)
+        if (!slot_k[s] || !slot_v[s])
+            return Q8A_E_INVAL;
+    if (st && st->magic == Q8A_STATE_MAGIC && n_kv_total > INT64_MAX / 4)
+        return Q8A_E_INVAL;
+    const int row = row_bytes(kv_dtype);
+    const int64_t head_stride = (int64_t)chunk_tokens * row;
+    int rc = check_chunk(st, q, slot_k[0], slot_v[0], kv_dtype, 0, chunk_tokens, head_stride,
+                         head_stride * (st ? st->n_heads : 1), causal);
+    if (rc)
+        return rc;
+    for (int s = 1; s < 2; ++s)
+        if (!aligned(slot_k[s], 16) || !aligned(slot_v[s], 16))
+            return Q8A_E_ALIGN;
+    const int64_t seq_stride = head_stride * st->n_heads;
+    const int64_t chunk_bytes = seq_stride * st->n_seq;
+    const int64_t n_chunks = (n_kv_total + chunk_tokens - 1) / chunk_tokens;
+    hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+    hipStream_t ds = static_cast<hipStream_t>(copy_stream);
+    const uint8_t *kh = static_cast<const uint8_t *>(k_host);
+    const uint8_t *vh = static_cast<const uint8_t *>(v_host);
+
+    hipEvent_t ev_full[2] = {nullptr, nullptr}, ev_free[2] = {nullptr, nullptr};
+    hipEvent_t ev_start = nullptr;
+    hipError_t e = hipSuccess;
+    auto destroy = [&]() {
+        for (int s = 0; s < 2; ++s) {
+            if (ev_full[s]) (void)hipEventDestroy(ev_full[s]);
+            if (ev_free[s]) (void)hipEventDestroy(ev_free[s]);
+        }
+        if (ev_start) (void)hipEventDestroy(ev_start);
+    };
+    for (int s = 0; s < 2 && e == hipSuccess; ++s) {
+        e = hipEventCreateWithFlags(&ev_full[s], hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&ev_free[s], hipEventDisableTiming);
+    }
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&ev_start, hipEventDisableTiming);
+    // the slots may still be read by earlier work on the compute stream
+    if (e == hipSuccess)
+        e = hipEventRecord(ev_start, cs);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(ds, ev_start, 0);
+    for (int64_t c = 0; c < n_chunks && e == hipSuccess; ++c) {
+        const int s = (int)(c & 1);
+        const int64_t kv_pos0 = c * chunk_tokens;
+        const int32_t n_kv = (int32_t)((n_kv_total - kv_pos0) < chunk_tokens
+                                           ? (n_kv_total - kv_pos0) : chunk_tokens);
+        if (c >= 2)
+            e = hipStreamWaitEvent(ds, ev_free[s], 0); // chunk c-2 has finished with slot s
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(slot_k[s], kh + c * chunk_bytes, (size_t)chunk_bytes,
+                               hipMemcpyHostToDevice, ds);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(slot_v[s], vh + c * chunk_bytes, (size_t)chunk_bytes,
+                               hipMemcpyHostToDevice, ds);
+        if (e == hipSuccess)
+            e = hipEventRecord(ev_full[s], ds);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(cs, ev_full[s], 0);
+        if (e == hipSuccess) {
+            q8a::AccumulateArgs a = make_args(st, q, slot_k[s], slot_v[s], kv_pos0, n_kv,
+                                              head_stride, seq_stride, causal);
+            e = q8a::launch_accumulate(a, kv_dtype, cs);
+        }
+        if (e == hipSuccess)
+            e = hipEventRecord(ev_free[s], cs);
+    }
+    destroy();
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
+} // extern "C"

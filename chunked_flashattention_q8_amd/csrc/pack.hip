@@ -1,0 +1,73 @@
+// Q8_0 pack kernel ("Core Architecture & The 4-Brick Pipeline", Sec. 5, block_q8_0: 32 int8
+// values plus one FP16 scale, 34 bytes, 8-bit symmetric).
+//
+// HBM-bound: each 32-value block reads 128 bytes and writes 34.  Eight consecutive lanes own one
+// block and each loads one 16-byte float4, so a wavefront reads 1 KiB of contiguous input per
+// instruction.  The block's largest magnitude is reduced over the eight lanes, every lane derives
+// the same FP16 scale, quantises its four values and writes them as two 16-bit stores (block
+// starts are 2-byte aligned: 34 * k).
+//
+// Arithmetic (bit-exact with the CPU oracle): d = amax / 127 with a correctly rounded FP32
+// division; d16 = FP16(d), round to nearest even; q = round(x / d16) with a correctly rounded
+// FP32 division and halves away from zero, clamped to [-127, 127]; an all-zero block gives
+// d16 = 0 and q = 0.
+#include <hip/hip_fp16.h>
+
+#include "q8attn_internal.h"
+
+namespace q8a {
+namespace {
+
+__device__ __forceinline__ int quantise(float x, float dh)
+{
+    if (dh == 0.0f)
+        return 0;
+    float r = roundf(__fdiv_rn(x, dh));
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict__ x,
+                                                         uint8_t *__restrict__ dst,
+                                                         int64_t n_blocks)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = gid >> 3;
+    const int sub = (int)(gid & 7);
+    const bool valid = blk < n_blocks;
+    float4 v = valid ? x[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 1, 8));
+    a = fmaxf(a, __shfl_xor(a, 2, 8));
+    a = fmaxf(a, __shfl_xor(a, 4, 8));
+
+    const __half d16 = __float2half_rn(__fdiv_rn(a, 127.0f));
+    const float dh = __half2float(d16);
+    const int q0 = quantise(v.x, dh), q1 = quantise(v.y, dh);
+    const int q2 = quantise(v.z, dh), q3 = quantise(v.w, dh);
+    if (!valid)
+        return;
+
+    uint8_t *out = dst + blk * 34;
+    if (sub == 0)
+        *reinterpret_cast<uint16_t *>(out) = __half_as_ushort(d16);
+    uint16_t *o16 = reinterpret_cast<uint16_t *>(out + 2 + 4 * sub);
+    o16[0] = (uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8));
+    o16[1] = (uint16_t)((q2 & 0xff) | ((q3 & 0xff) << 8));
+}
+
+} // namespace
+
+hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s)
+{
+    if (n_blocks == 0)
+        return hipSuccess;
+    const int64_t threads = n_blocks * 8;
+    const int64_t grid = (threads + 255) / 256;
+    hipLaunchKernelGGL(q8_0_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(x), dst, n_blocks);
+    return hipGetLastError();
+}
+
+} // namespace q8a

@@ -1,0 +1,35 @@
+// Internal declarations shared by the translation units of libq8attn.so (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8a {
+
+constexpr int kHeadDim = 64;
+constexpr int kQ8RowBytes = 68;   // two 34-byte Q8_0 blocks per 64-dim head row
+constexpr int kF16RowBytes = 128; // 64 FP16 values
+
+// Arguments of one accumulate launch: the chunk of keys [kv_pos0, kv_pos0 + n_kv) of every
+// (sequence, head) pair, applied to the state rows of that pair.
+struct AccumulateArgs {
+    const void *q;          // FP16 [B][H][M][64]
+    const uint8_t *k;       // key 0 of sequence 0, head 0
+    const uint8_t *v;
+    float *m, *l, *o;       // state
+    int64_t kv_head_stride; // bytes
+    int64_t kv_seq_stride;  // bytes
+    int64_t q_pos0;
+    int64_t kv_pos0;
+    int32_t B, H, M;
+    int32_t n_kv;
+    int32_t causal;
+};
+
+hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s);
+hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s);
+hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s);
+hipError_t launch_finalize(const float *m, const float *l, const float *o, void *out,
+                           float *lse, int64_t n_rows, hipStream_t s);
+
+} // namespace q8a

@@ -1,0 +1,137 @@
+/*
+ * q8attn.h -- exact chunked causal attention prefill over a Q8_0 KV cache, for AMD MI355X (gfx950).
+ *
+ * The method ("Out-of-Core Flash Streaming & Speculative Decode (1M Context)", m4-prefill-engine,
+ * Sec. 3 "Chunked FlashAttention: Exact Mathematical Derivation"): the KV sequence arrives in
+ * chunks; for every query row i the running state (m_i, l_i, O_i) -- the largest scaled logit seen
+ * so far, the sum of e^(S_ij - m_i), and the unnormalised output sum of e^(S_ij - m_i) V_j -- is
+ * kept in device memory between chunk calls and updated with the rescale factor
+ * e^(m_old - m_new), so that O/l after the last chunk equals single-pass softmax(QK^T/sqrt(D)) V.
+ * Keys and values are stored as Q8_0 ("Core Architecture & The 4-Brick Pipeline", Sec. 5,
+ * block_q8_0): blocks of 32 values, each an FP16 scale followed by 32 int8, 34 bytes; a 64-dim
+ * head row is two blocks, 68 bytes.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless the name ends in _host.  The caller owns every buffer
+ *     and every stream and keeps buffers alive until the enqueued work has completed.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL = the legacy
+ *     default stream).  No call allocates or frees device memory or synchronises the host.
+ *   - All argument checks run on the host before anything is enqueued; on failure nothing is
+ *     launched and the state descriptor is unchanged.  A failing HIP runtime call (for example
+ *     no device) returns Q8A_E_HIP and its hipError_t is kept for q8a_last_hip_error().  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - head_dim must be 64.  Layouts are head-major: Q and the output [B][H][M][64] FP16,
+ *     state m and l [B][H][M] FP32, state O [B][H][M][64] FP32.  Query row i of every sequence
+ *     sits at absolute position q_pos0 + i; chunk key j at absolute position kv_pos0 + j.
+ *   - Causal rule: a query at position p sees the keys at positions <= p (diagonal included).
+ *   - Supported value range: finite inputs with |x| < 30000 for K and V (larger Q8_0 scales can
+ *     overflow FP16 intermediates); scores are computed in FP32.
+ */
+#ifndef Q8ATTN_H
+#define Q8ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8A_OK = 0,
+    Q8A_E_INVAL = 1,       /* bad pointer, size, position or enum value */
+    Q8A_E_UNSUPPORTED = 2, /* a valid request this library does not implement (e.g. head_dim) */
+    Q8A_E_ALIGN = 3,       /* a pointer or stride breaks the stated alignment */
+    Q8A_E_STATE = 4,       /* descriptor not initialised, or it does not match the call */
+    Q8A_E_HIP = 5          /* a HIP runtime call failed; see q8a_last_hip_error() */
+} q8a_status;
+
+typedef enum {
+    Q8A_KV_Q8_0 = 0, /* K and V rows of 68 bytes: [fp16 d0][32 x int8][fp16 d1][32 x int8] */
+    Q8A_KV_F16 = 1   /* K and V rows of 64 FP16 values (128 bytes) */
+} q8a_kv_dtype;
+
+#define Q8A_STATE_MAGIC 0x51384154u /* "Q8AT" */
+
+/* Host-side descriptor of a caller-owned online-softmax state.  Filled by attn_state_init; the
+ * other calls only read it.  A state row whose m is -inf is EMPTY: it has seen no key, its l is 0
+ * and its O is treated as zero and never read (so O need not be cleared). */
+typedef struct {
+    float *m;          /* [n_seq][n_heads][n_q]      running maximum of the scaled logits  */
+    float *l;          /* [n_seq][n_heads][n_q]      running sum of e^(S - m)             */
+    float *o;          /* [n_seq][n_heads][n_q][64]  running sum of e^(S - m) V           */
+    int32_t n_seq, n_heads, n_q, head_dim;
+    int64_t q_pos0;    /* absolute position of query row 0 (same for every sequence) */
+    uint32_t magic;    /* Q8A_STATE_MAGIC once initialised */
+    uint32_t flags;    /* reserved, 0 */
+} q8a_state;
+
+/* Q8_0 pack ("Core Architecture & The 4-Brick Pipeline", Sec. 5, block_q8_0; row size from
+ * "Out-of-Core Flash Streaming ...", Sec. 1).
+ *   x       FP32 [n_rows][row_len], C-contiguous, 16-byte aligned.
+ *   dst     n_rows * row_len/32 * 34 bytes, 2-byte aligned; block k of the flat sequence at byte
+ *           34*k: the FP16 scale (little-endian) then 32 int8.
+ *   row_len positive multiple of 32 (64 for a KV head row); n_rows >= 0 (0 enqueues nothing).
+ * Per block: amax = max|x|, d = amax/127 (FP32, correctly rounded), d16 = FP16(d) (round to
+ * nearest even), q = round(x / d16) (FP32 division, halves away from zero), clamped to
+ * [-127, 127]; an all-zero block stores d16 = 0 and q = 0.  Bit-exact with the CPU oracle. */
+int q8_0_pack(const float *x, void *dst, int64_t n_rows, int32_t row_len, void *stream);
+
+/* Describe a state and make every row empty: writes m = -inf and l = 0 for all
+ * n_seq*n_heads*n_q rows (O is not written; see q8a_state).
+ *   m, l    FP32 [n_seq][n_heads][n_q], 4-byte aligned;  o  FP32 [...][64], 16-byte aligned.
+ *   head_dim must be 64 (else Q8A_E_UNSUPPORTED); n_seq, n_heads, n_q >= 1; q_pos0 >= 0. */
+int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
+                    int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0,
+                    void *stream);
+
+/* Accumulate one KV chunk into the state (the recurrence of "Out-of-Core Flash Streaming ...",
+ * Sec. 3, steps 1-6).
+ *   q        FP16 [n_seq][n_heads][n_q][64], 16-byte aligned (same Q on every call).
+ *   k, v     address of key 0 of the chunk for sequence 0, head 0.  Key j of (seq b, head h) is
+ *            at  k + b*kv_seq_stride + h*kv_head_stride + j*row  (row = 68 bytes for Q8_0,
+ *            128 for FP16).  16-byte aligned; both strides are byte counts, multiples of 16,
+ *            and at least n_kv*row.
+ *   kv_pos0  absolute position of chunk key 0 (>= 0);  n_kv  chunk length, >= 1 (a partial
+ *            last chunk is fine).
+ *   causal   1: the triangular mask of Mode A ("Out-of-Core ...", Sec. 4); 0: every chunk key
+ *            is visible to every query.
+ * A row that sees no key of the chunk is left bit-for-bit untouched (tiles that lie wholly above
+ * the diagonal are skipped, as in "Core Architecture ...", Sec. 5).  Each key position must be
+ * accumulated exactly once per state; chunk order is free.  Calls on one state must be
+ * stream-ordered; calls on different states are independent. */
+int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, const void *v,
+                          int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
+                          int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
+                          void *stream);
+
+/* Final output after the last chunk ("Out-of-Core ...", Sec. 3): out = O / l rounded once to
+ * FP16 (nearest even), and lse = m + ln(l) in FP32 (natural log).  Empty rows give out = 0 and
+ * lse = -inf.  out: FP16 [n_seq][n_heads][n_q][64], 16-byte aligned; lse: FP32 [..][n_q] or NULL.
+ * The state is not modified. */
+int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream);
+
+/* Double-buffered streaming of a KV cache held in pinned host memory ("Out-of-Core ...", Sec. 2:
+ * two ping-pong slots, chunk c+1 copied while chunk c is computed, handoff by synchronisation
+ * objects rather than spinning).  Chunk c of the cache covers key positions
+ * [c*chunk_tokens, min((c+1)*chunk_tokens, n_kv_total)); its bytes sit at
+ * k_host + c*chunk_bytes, laid out [n_seq][n_heads][chunk_tokens][row] (the last chunk padded),
+ * chunk_bytes = n_seq*n_heads*chunk_tokens*row.  slot_k[2], slot_v[2] are device buffers of
+ * chunk_bytes each, 16-byte aligned.  Copies run on copy_stream (hipMemcpyAsync host->device),
+ * kernels on compute_stream; HIP events order slot reuse.  On return everything is enqueued;
+ * compute_stream carries the completion of the last chunk.  Key positions start at 0. */
+int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_host,
+                           const void *v_host, int32_t kv_dtype, int64_t n_kv_total,
+                           int32_t chunk_tokens, void *const slot_k[2], void *const slot_v[2],
+                           int32_t causal, void *compute_stream, void *copy_stream);
+
+/* Human-readable name of a q8a_status value. */
+const char *q8a_status_string(int status);
+
+/* hipError_t of the most recent Q8A_E_HIP returned on the calling thread (0 if none). */
+int q8a_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8ATTN_H */

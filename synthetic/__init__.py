@@ -17,17 +17,21 @@ id    name                B   H   M      N          q_pos0     B_C      checked
 4     stream_1m           1   32  2048   1048576    1046528    16384    32/head
 ====  ==================  ==  ==  =====  =========  =========  =======  =========
 
-Draws: for workload k, Q comes from ``torch.Generator().manual_seed(1000*k + 1)``, K from
-seed ``1000*k + 2`` and V from ``1000*k + 3``, each ``torch.randn`` in float32 of the full
-[B, H, rows, 64] shape.  Q is then stored as FP16 (round to nearest even) because the method's
-queries are FP16; K and V stay float32 (they are quantised by the method).  The streamed
-1M-token workload draws K then V per chunk c from seed ``4000 + 10 + c`` with shape
-[H, B_C, 64], so no process ever holds the whole float32 cache.  Sampled query rows come from
-``numpy.random.default_rng(1000*k + 9)``, drawn per head without replacement, always including
-rows 0 and M - 1.
+Draws: every tensor is a stack of [rows, 64] slices, one per (sequence, head); slice i of a
+tensor with seed s is filled by ``torch.Tensor.normal_`` (float32, mean 0, std 1) from its own
+``torch.Generator`` seeded ``s * 1_000_003 + i``, so slices can be drawn on parallel threads and
+the values do not depend on the thread count.  For workload k, Q uses seed ``1000*k + 1``, K
+``1000*k + 2`` and V ``1000*k + 3``.  Q is then stored as FP16 (round to nearest even) because
+the method's queries are FP16; K and V stay float32 (they are quantised by the method).  The
+streamed 1M-token workload draws K and V per chunk c with seeds ``1000*k + 100 + 2c`` and
+``1000*k + 101 + 2c`` and shape [H, B_C, 64], so no process ever holds the whole float32 cache.
+Sampled query rows come from ``numpy.random.default_rng(1000*k + 9)``, drawn per head without
+replacement, always including rows 0 and M - 1.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -84,9 +88,30 @@ def _gen(seed: int) -> torch.Generator:
     return g
 
 
+def _fill_slice(out: torch.Tensor, i: int, seed: int) -> None:
+    out[i].normal_(generator=_gen(seed * 1_000_003 + i))
+
+
 def randn(shape, seed: int) -> np.ndarray:
-    """float32 N(0, 1) draws, C-contiguous numpy array."""
-    return torch.randn(tuple(shape), generator=_gen(seed), dtype=torch.float32).numpy()
+    """float32 N(0, 1) draws of the given shape [..., rows, 64], C-contiguous numpy array."""
+    shape = tuple(int(d) for d in shape)
+    out = torch.empty(shape, dtype=torch.float32)
+    flat = out.view((-1,) + shape[-2:])
+    n = flat.shape[0]
+    if n == 1 or flat[0].numel() < (1 << 16):
+        for i in range(n):
+            _fill_slice(flat, i, seed)
+    else:
+        with ThreadPoolExecutor(max_workers=min(n, _workers())) as ex:
+            list(ex.map(lambda i: _fill_slice(flat, i, seed), range(n)))
+    return out.numpy()
+
+
+def _workers() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return 4
 
 
 def to_f16_bits(x: np.ndarray) -> np.ndarray:
@@ -110,10 +135,9 @@ def gen_kv(w: Workload):
 def gen_kv_chunk(w: Workload, c: int):
     """Float32 K and V of chunk c of a streamed workload, [H, n_kv, 64] each (B = 1)."""
     kv_pos0, n_kv = w.chunks()[c]
-    g = _gen(1000 * w.wid + 10 + c)
-    k = torch.randn((w.H, n_kv, w.D), generator=g, dtype=torch.float32).numpy()
-    v = torch.randn((w.H, n_kv, w.D), generator=g, dtype=torch.float32).numpy()
-    return k, v
+    shape = (w.H, n_kv, w.D)
+    return (randn(shape, 1000 * w.wid + 100 + 2 * c),
+            randn(shape, 1000 * w.wid + 101 + 2 * c))
 
 
 def sample_rows(w: Workload, rows_per_head: int | None = None) -> np.ndarray:

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function the
+header declares, and each invalid argument is rejected with its status before anything is
+enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import chunked_flashattention_q8_amd as q8a
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8attn.h")
+NO_GPU = torch.cuda.device_count() == 0
+
+# fake device addresses: never dereferenced, because every call below fails validation first
+A16 = 0x10000
+A16B = 0x20000
+A16C = 0x30000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert set(names) == set(q8a.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q8a.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert q8a.status_string(0) == "ok"
+    for s in range(1, 6):
+        assert q8a.status_string(s) != "unknown status"
+    assert q8a.status_string(99) == "unknown status"
+
+
+def rc_of(fn):
+    try:
+        fn()
+    except q8a.Q8AError as e:
+        return e.status
+    return q8a.Q8A_OK
+
+
+def test_pack_rejects_bad_arguments():
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    assert lib.q8_0_pack(P(A16), P(A16B), -1, 64, None) == q8a.Q8A_E_INVAL
+    assert lib.q8_0_pack(P(A16), P(A16B), 4, 48, None) == q8a.Q8A_E_INVAL
+    assert lib.q8_0_pack(P(A16), P(A16B), 4, 0, None) == q8a.Q8A_E_INVAL
+    assert lib.q8_0_pack(None, P(A16B), 4, 64, None) == q8a.Q8A_E_INVAL
+    assert lib.q8_0_pack(P(A16 + 4), P(A16B), 4, 64, None) == q8a.Q8A_E_ALIGN
+    assert lib.q8_0_pack(P(A16), P(A16B + 1), 4, 64, None) == q8a.Q8A_E_ALIGN
+    assert lib.q8_0_pack(P(A16), P(A16B), 0, 64, None) == q8a.Q8A_OK  # nothing to do
+
+
+def test_state_init_rejects_bad_arguments():
+    lib = q8a.library()
+    st = q8a.q8a_state()
+    P = ctypes.c_void_p
+    ok = (P(A16), P(A16B), P(A16C))
+    assert lib.attn_state_init(ctypes.byref(st), *ok, 1, 4, 256, 128, 0, None) == \
+        q8a.Q8A_E_UNSUPPORTED
+    assert lib.attn_state_init(ctypes.byref(st), *ok, 0, 4, 256, 64, 0, None) == q8a.Q8A_E_INVAL
+    assert lib.attn_state_init(ctypes.byref(st), *ok, 1, 4, 256, 64, -1, None) == \
+        q8a.Q8A_E_INVAL
+    assert lib.attn_state_init(ctypes.byref(st), P(A16), P(A16B), P(A16C + 8), 1, 4, 256, 64,
+                               0, None) == q8a.Q8A_E_ALIGN
+    assert lib.attn_state_init(None, *ok, 1, 4, 256, 64, 0, None) == q8a.Q8A_E_INVAL
+    assert st.magic == 0  # untouched on failure
+
+
+def fake_state(B=1, H=4, M=256):
+    st = q8a.q8a_state()
+    st.m, st.l, st.o = A16, A16B, A16C
+    st.n_seq, st.n_heads, st.n_q, st.head_dim = B, H, M, 64
+    st.q_pos0 = 0
+    st.magic = q8a.STATE_MAGIC
+    return st
+
+
+def acc(st, q=A16, k=A16B, v=A16C, dtype=0, pos=0, n=64, hs=None, ss=0, causal=1):
+    if hs is None:
+        hs = 256 * 68
+    P = ctypes.c_void_p
+    return q8a.library().attn_accumulate_chunk(ctypes.byref(st), P(q), P(k), P(v), dtype, pos,
+                                               n, hs, ss, causal, None)
+
+
+def test_accumulate_rejects_bad_arguments():
+    st = fake_state()
+    assert acc(q8a.q8a_state()) == q8a.Q8A_E_STATE          # not initialised
+    bad = fake_state()
+    bad.head_dim = 128
+    assert acc(bad) == q8a.Q8A_E_STATE
+    assert acc(st, dtype=7) == q8a.Q8A_E_INVAL
+    assert acc(st, n=0) == q8a.Q8A_E_INVAL
+    assert acc(st, pos=-1) == q8a.Q8A_E_INVAL
+    assert acc(st, causal=2) == q8a.Q8A_E_INVAL
+    assert acc(st, q=0) == q8a.Q8A_E_INVAL
+    assert acc(st, hs=64 * 68 - 16) == q8a.Q8A_E_INVAL      # head stride shorter than a chunk
+    assert acc(st, hs=-16) == q8a.Q8A_E_INVAL
+    assert acc(st, n=40_000_000) == q8a.Q8A_E_INVAL         # beyond the 32-bit byte range
+    assert acc(st, k=A16B + 4) == q8a.Q8A_E_ALIGN
+    assert acc(st, q=A16 + 8) == q8a.Q8A_E_ALIGN
+    assert acc(st, hs=256 * 68 + 4) == q8a.Q8A_E_ALIGN
+    st2 = fake_state(B=2)
+    assert acc(st2, ss=0) == q8a.Q8A_E_INVAL                # sequences would overlap
+
+
+def test_finalize_rejects_bad_arguments():
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    st = fake_state()
+    assert lib.attn_finalize(ctypes.byref(q8a.q8a_state()), P(A16), None, None) == \
+        q8a.Q8A_E_STATE
+    assert lib.attn_finalize(ctypes.byref(st), None, None, None) == q8a.Q8A_E_INVAL
+    assert lib.attn_finalize(ctypes.byref(st), P(A16 + 2), None, None) == q8a.Q8A_E_ALIGN
+    assert lib.attn_finalize(ctypes.byref(st), P(A16), P(A16B + 1), None) == q8a.Q8A_E_ALIGN
+
+
+def test_stream_rejects_bad_arguments():
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    st = fake_state(H=2, M=64)
+    slots = (P * 2)(A16B, A16C)
+    slots_bad = (P * 2)(A16B, None)
+    args = dict(q=P(A16), kh=P(0x40000), vh=P(0x50000))
+
+    def call(st_, sk, sv, n_total=1000, chunk=256, dtype=0):
+        return lib.attn_accumulate_stream(ctypes.byref(st_), args["q"], args["kh"], args["vh"],
+                                          dtype, n_total, chunk, sk, sv, 1, None, None)
+    assert call(st, slots, slots_bad) == q8a.Q8A_E_INVAL
+    assert call(st, slots, slots, n_total=0) == q8a.Q8A_E_INVAL
+    assert call(st, slots, slots, chunk=0) == q8a.Q8A_E_INVAL
+    assert call(q8a.q8a_state(), slots, slots) == q8a.Q8A_E_STATE
+    assert call(st, slots, slots, dtype=3) == q8a.Q8A_E_INVAL
+    assert call(st, (P * 2)(A16B, A16C + 8), slots) == q8a.Q8A_E_ALIGN
+
+
+@pytest.mark.skipif(not NO_GPU, reason="needs a host without a GPU")
+def test_valid_call_without_device_reports_hip_error():
+    """On a host with no GPU, a call that passes validation fails in the HIP runtime and says so
+    (Q8A_E_HIP plus the hipError_t), instead of falling back to the CPU."""
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    rc = lib.q8_0_pack(P(A16), P(A16B), 4, 64, None)
+    assert rc == q8a.Q8A_E_HIP
+    assert lib.q8a_last_hip_error() != 0

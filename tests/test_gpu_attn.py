@@ -1,0 +1,220 @@
+"""GPU chunked causal attention against the FP64 oracle, element by element, through the C ABI.
+
+Small cases span several 128-query workgroups and 64-key tiles and end in ragged tails (query
+counts that leave partial wavefronts, chunk lengths whose byte size is not a multiple of 16);
+the edge cases are a single key, chunks no query can see, non-causal chunks, shuffled chunk
+order, checkpoint/resume and the empty state."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_flashattention_q8_amd as q8a
+import synthetic
+from gpu_util import (D, assert_close, f16_to_dev, gpu_pack, metrics, prefill, rows_of, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_case(orc, B, H, M, N, q_pos0, seed, kv_dtype=q8a.KV_Q8_0):
+    q, k, v = synthetic.small_case(B, H, M, N, q_pos0, seed)
+    qd = f16_to_dev(q)
+    if kv_dtype == q8a.KV_Q8_0:
+        kd, vd = gpu_pack(k), gpu_pack(v)
+        kb, vb = orc.q8_0_pack(k), orc.q8_0_pack(v)
+        torch.cuda.synchronize()
+        assert np.array_equal(kd.cpu().numpy(), kb) and np.array_equal(vd.cpu().numpy(), vb)
+        prob = orc.Problem(q, kb, vb, orc.KV_Q8_0, q_pos0)
+    else:
+        kb, vb = synthetic.to_f16_bits(k), synthetic.to_f16_bits(v)
+        kd, vd = f16_to_dev(kb), f16_to_dev(vb)
+        prob = orc.Problem(q, kb, vb, orc.KV_F16, q_pos0)
+    return prob, qd, kd, vd
+
+
+def chunk_list(N, bc):
+    return [(s, min(bc, N - s)) for s in range(0, N, bc)]
+
+
+CASES = [
+    # B, H, M, N, q_pos0, chunk, causal.  The cache holds N rounded up to a multiple of 4 keys
+    # (so head strides are 16-byte multiples); the chunks cover keys [0, N).
+    (1, 2, 200, 200, 0, 64, 1),       # ragged query tile and wavefront, ragged last tile
+    (2, 3, 130, 333, 203, 100, 1),    # last chunk of 33 keys: 2244 bytes, not a 16-multiple
+    (1, 1, 1, 1, 0, 1, 1),            # one query, one key
+    (1, 2, 31, 97, 66, 12, 1),        # fewer rows than a wavefront, many small chunks
+    (1, 2, 64, 1000, 936, 1000, 1),   # one chunk, queries at the end of a longer cache
+    (1, 2, 100, 152, 0, 52, 0),       # non-causal
+    (1, 2, 40, 500, 0, 128, 1),       # chunks after every query position: no row touched
+    (3, 1, 384, 384, 0, 384, 1),      # three sequences, full diagonal in one chunk
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_small_cases(orc, case):
+    B, H, M, N, q_pos0, bc, causal = case
+    say("case", case)
+    n_alloc = (N + 3) // 4 * 4
+    assert causal or n_alloc == N  # without the mask every allocated key would be visible
+    prob, qd, kd, vd = setup_case(orc, B, H, M, n_alloc, q_pos0, seed=sum(case))
+    prob.causal = bool(causal)
+    out, lse, _ = prefill(qd, kd, vd, q8a.KV_Q8_0, B, H, M, n_alloc, q_pos0,
+                          chunk_list(N, bc), causal)
+    O_ref, lse_ref = orc.attention(prob)
+    assert_close(out.float().cpu().numpy().reshape(-1, D), lse.cpu().numpy().reshape(-1),
+                 O_ref, lse_ref, str(case))
+
+
+def test_fp16_kv_small(orc):
+    B, H, M, N, q_pos0 = 2, 2, 150, 260, 110
+    say("fp16 kv")
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=77, kv_dtype=q8a.KV_F16)
+    out, lse, _ = prefill(qd, kd, vd, q8a.KV_F16, B, H, M, N, q_pos0, chunk_list(N, 80))
+    O_ref, lse_ref = orc.attention(prob)
+    assert_close(out.float().cpu().numpy().reshape(-1, D), lse.cpu().numpy().reshape(-1),
+                 O_ref, lse_ref, "fp16")
+
+
+def test_state_after_every_chunk(orc):
+    """After each call the state matches the oracle's recurrence state: same non-empty rows,
+    m to FP32 accuracy, and the running softmax O/l and m + ln l within the output bounds."""
+    B, H, M, N, q_pos0, bc = 1, 4, 256, 256, 0, 64
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=100)
+    ref = [None]
+
+    def on_state(s, n, m, l, o):
+        ref[0] = orc.attention_chunks(prob, [(s, n)], state=ref[0])
+        m_ref, l_ref, O_ref = ref[0]
+        mg, lg = m.cpu().numpy().reshape(-1), l.cpu().numpy().reshape(-1)
+        og = o.cpu().numpy().reshape(-1, D)
+        empty = np.isneginf(m_ref)
+        assert np.array_equal(np.isneginf(mg), empty)
+        assert not lg[empty].any()
+        ne = ~empty
+        assert np.all(np.abs(mg[ne] - m_ref[ne]) <= 1e-5 * np.maximum(1, np.abs(m_ref[ne])))
+        assert_close(og[ne] / lg[ne, None], mg[ne] + np.log(lg[ne]),
+                     O_ref[ne] / l_ref[ne, None], m_ref[ne] + np.log(l_ref[ne]),
+                     "state after chunk at %d" % s)
+
+    prefill(qd, kd, vd, q8a.KV_Q8_0, B, H, M, N, q_pos0, chunk_list(N, bc), on_state=on_state)
+
+
+def test_rows_without_visible_keys_are_untouched(orc):
+    B, H, M, N, q_pos0 = 1, 2, 256, 512, 0
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=5)
+    m, l, o = q8a.alloc_state(B, H, M)
+    st = q8a.attn_state_init(m, l, o, B, H, M, D, q_pos0)
+    q8a.attn_accumulate_chunk(st, qd, kd, vd, 0, 0, 192, N * 68, H * N * 68, 1)
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (m, l, o)]
+    # keys 256..511 come after every query position
+    q8a.attn_accumulate_chunk(st, qd, kd.data_ptr() + 256 * 68, vd.data_ptr() + 256 * 68, 0,
+                              256, 256, N * 68, H * N * 68, 1)
+    torch.cuda.synchronize()
+    for a, b in zip(before, (m, l, o)):
+        assert torch.equal(a, b)
+    # keys 192..255: rows 0..191 see none of them and stay bit-identical
+    q8a.attn_accumulate_chunk(st, qd, kd.data_ptr() + 192 * 68, vd.data_ptr() + 192 * 68, 0,
+                              192, 64, N * 68, H * N * 68, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(before[0][..., :192], m[..., :192])
+    assert torch.equal(before[2][..., :192, :], o[..., :192, :])
+    assert not torch.equal(before[2][..., 192:, :], o[..., 192:, :])
+
+
+def test_shuffled_chunk_order(orc):
+    B, H, M, N, q_pos0 = 1, 3, 300, 640, 340
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=9)
+    chunks = chunk_list(N, 64)
+    order = np.random.default_rng(1).permutation(len(chunks))
+    out, lse, _ = prefill(qd, kd, vd, 0, B, H, M, N, q_pos0, [chunks[i] for i in order])
+    O_ref, lse_ref = orc.attention(prob)
+    assert_close(out.float().cpu().numpy().reshape(-1, D), lse.cpu().numpy().reshape(-1),
+                 O_ref, lse_ref, "shuffled")
+
+
+def test_deterministic_and_resumable(orc):
+    B, H, M, N, q_pos0 = 2, 2, 256, 512, 256
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=21)
+    chunks = chunk_list(N, 128)
+    out1, lse1, _ = prefill(qd, kd, vd, 0, B, H, M, N, q_pos0, chunks)
+    out2, lse2, _ = prefill(qd, kd, vd, 0, B, H, M, N, q_pos0, chunks)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    # checkpoint after two chunks, clobber the device state, restore, finish
+    m, l, o = q8a.alloc_state(B, H, M)
+    st = q8a.attn_state_init(m, l, o, B, H, M, D, q_pos0)
+    prefill(qd, kd, vd, 0, B, H, M, N, q_pos0, chunks[:2], state=(st, (m, l, o)))
+    saved = [t.cpu() for t in (m, l, o)]
+    for t in (m, l, o):
+        t.fill_(float("nan"))
+    for t, s in zip((m, l, o), saved):
+        t.copy_(s)
+    out3, lse3, _ = prefill(qd, kd, vd, 0, B, H, M, N, q_pos0, chunks[2:], state=(st, (m, l, o)))
+    assert torch.equal(out1, out3) and torch.equal(lse1, lse3)
+
+
+def test_empty_state_finalize():
+    B, H, M = 1, 2, 100
+    m, l, o = q8a.alloc_state(B, H, M)
+    o.fill_(float("nan"))  # an empty row's O is never read
+    st = q8a.attn_state_init(m, l, o, B, H, M, D, 0)
+    out = torch.full((B, H, M, D), 7.0, dtype=torch.float16, device="cuda")
+    lse = torch.zeros((B, H, M), dtype=torch.float32, device="cuda")
+    q8a.attn_finalize(st, out, lse)
+    torch.cuda.synchronize()
+    assert not out.any()
+    assert torch.all(torch.isneginf(lse))
+
+
+# ---------------------------------------------------------------- the workloads' own shapes
+
+def run_workload(orc, wid, kv_dtype=q8a.KV_Q8_0, chunk=None, rows_per_head=None):
+    w = synthetic.WORKLOADS[wid]
+    say("workload", w.name, "dtype", kv_dtype, "chunk", chunk or w.chunk)
+    q = synthetic.gen_q(w)
+    k, v = synthetic.gen_kv(w)
+    qd = f16_to_dev(q)
+    if kv_dtype == q8a.KV_Q8_0:
+        kb, vb = orc.q8_0_pack(k), orc.q8_0_pack(v)
+        kd, vd = gpu_pack(k), gpu_pack(v)
+        torch.cuda.synchronize()
+        assert np.array_equal(kd.cpu().numpy(), kb) and np.array_equal(vd.cpu().numpy(), vb)
+        prob = orc.Problem(q, kb, vb, orc.KV_Q8_0, w.q_pos0)
+    else:
+        kb, vb = synthetic.to_f16_bits(k), synthetic.to_f16_bits(v)
+        kd, vd = f16_to_dev(kb), f16_to_dev(vb)
+        prob = orc.Problem(q, kb, vb, orc.KV_F16, w.q_pos0)
+    del k, v
+    bc = chunk or w.chunk
+    out, lse, _ = prefill(qd, kd, vd, kv_dtype, w.B, w.H, w.M, w.N, w.q_pos0,
+                          [(s, min(bc, w.N - s)) for s in range(0, w.N, bc)])
+    rows = synthetic.sample_rows(w, rows_per_head)
+    O_ref, lse_ref = orc.attention(prob, rows)
+    return assert_close(rows_of(out, rows, D), rows_of(lse, rows), O_ref, lse_ref, w.name)
+
+
+def test_workload_tiny(orc):
+    run_workload(orc, 0)
+
+
+def test_workload_incore_m2048(orc):
+    run_workload(orc, 1)
+
+
+@pytest.mark.timeout(300)
+def test_workload_batch8_q8_0(orc):
+    run_workload(orc, 2)
+
+
+@pytest.mark.timeout(300)
+def test_workload_batch8_f16(orc):
+    run_workload(orc, 2, kv_dtype=q8a.KV_F16)
+
+
+@pytest.mark.timeout(300)
+def test_workload_batch8_one_chunk(orc):
+    run_workload(orc, 2, chunk=2048)
+
+
+@pytest.mark.timeout(300)
+def test_workload_append_133k(orc):
+    run_workload(orc, 3)

@@ -1,0 +1,56 @@
+"""GPU q8_0_pack is bit-exact with the oracle's Q8_0 codec ("Core Architecture & The 4-Brick
+Pipeline", Sec. 5, block_q8_0)."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_flashattention_q8_amd as q8a
+import synthetic
+from gpu_util import dev, gpu_pack, say
+
+pytestmark = pytest.mark.gpu
+
+
+def pack_rows(x: np.ndarray, row_len: int) -> np.ndarray:
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    n_rows = x.size // row_len
+    out = torch.empty(n_rows * row_len // 32 * 34, dtype=torch.uint8, device=dev())
+    q8a.q8_0_pack(xt, out, n_rows, row_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(x.shape[:-1] + (row_len // 32 * 34,))
+
+
+@pytest.mark.parametrize("n_rows,row_len", [(1, 32), (3, 64), (1001, 64), (257, 96), (40000, 64)])
+def test_pack_random_bitexact(orc, n_rows, row_len):
+    rng = np.random.default_rng(n_rows)
+    x = rng.standard_normal((n_rows, row_len)).astype(np.float32)
+    x *= np.exp2(rng.uniform(-6, 9, size=(n_rows, 1))).astype(np.float32)
+    say("pack", n_rows, row_len)
+    assert np.array_equal(pack_rows(x, row_len), orc.q8_0_pack(x))
+
+
+def test_pack_ties_zero_blocks_and_exact_scales(orc):
+    rng = np.random.default_rng(5)
+    blocks = []
+    for s in (1.0, 0.5, 0.0078735352, 3.0, 2.0 ** -9):
+        s = float(np.float16(s))
+        k = rng.integers(-126, 126, size=(64, 32)) + 0.5 * (rng.random((64, 32)) < 0.5)
+        k[:, 0] = 127
+        blocks.append((k * s).astype(np.float32))
+    blocks.append(np.zeros((8, 32), dtype=np.float32))
+    tiny = rng.standard_normal((16, 32)).astype(np.float32) * np.float32(1e-3)  # subnormal d16
+    blocks.append(tiny)
+    x = np.concatenate(blocks).reshape(-1, 64)
+    say("pack special blocks", x.shape)
+    assert np.array_equal(pack_rows(x, 64), orc.q8_0_pack(x))
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2])
+def test_pack_workload_kv(orc, wid):
+    w = synthetic.WORKLOADS[wid]
+    k, v = synthetic.gen_kv(w)
+    for name, x in (("K", k), ("V", v)):
+        say("pack workload", wid, name, x.shape)
+        got = gpu_pack(x)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), orc.q8_0_pack(x)), name
