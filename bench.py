@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked causal attention prefill over a Q8_0 KV cache on one MI355X.
+
+Prints ONE JSON line on stdout.  A step is one pass of the whole hot path over one batch of
+synthetic input that is already resident in HBM: Q8_0 pack of K and V (FP32 in, 68-byte rows
+out), state init, one attn_accumulate_chunk call per chunk, finalize.  The default workload is
+8 sequences x 32 heads x 2048 causal queries over 2048 keys, head_dim 64, chunks of 512 keys
+(four chunk calls): the M = 2048, 32-head Q8_0 prefill.
+
+value     = causal attention FLOPs per step (4 * 64 per visible (query, key) pair per head) /
+            step time, in TFLOP/s.
+roofline  = the accumulate kernel (the dominant one): algorithmic FLOPs per launch / its mean
+            launch duration from HIP events on the launch stream, against the dense FP16 MFMA
+            peak of MI355X (2.5 PFLOP/s).  traffic = HBM bytes per launch from rocprofv3
+            FETCH_SIZE / WRITE_SIZE counters (scaled by a plain-copy calibration), read from
+            profiles/ and reported only if the kernel source is unchanged since.
+cpu_baseline = the FP64 CPU oracle (pack + single-pass attention) on whole heads of the same
+            workload, for about --cpu-seconds of host time; its outputs also check the GPU
+            output of those heads.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill attention TFLOP/s & % of MI355X FP16 MFMA peak (Q8_0 KV)"
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16 MFMA
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "accumulate_batch8_m2048_traffic.json")
+KERNEL_SOURCES = ["chunked_flashattention_q8_amd/csrc/attn.hip",
+                  "chunked_flashattention_q8_amd/csrc/q8attn_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def chunk_flops(w, kv_pos0, n_kv):
+    """Algorithmic FLOPs of one chunk call: 256 per visible (query, key) pair per head."""
+    import numpy as np
+    pos = w.q_pos0 + np.arange(w.M, dtype=np.int64)
+    vis = np.clip(pos - kv_pos0 + 1, 0, n_kv)
+    return int(vis.sum()) * w.B * w.H * 4 * w.D
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, for calibrating HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+
+
+def run_resident(w, kv_dtype, chunk, steps, warmup):
+    import numpy as np
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    q = synthetic.gen_q(w)
+    k, v = synthetic.gen_kv(w)
+    qd = torch.from_numpy(q).view(torch.float16).to(dev)
+    if kv_dtype == q8a.KV_Q8_0:
+        kx = torch.from_numpy(k).to(dev)
+        vx = torch.from_numpy(v).to(dev)
+        kd = torch.empty((w.B, w.H, w.N, 68), dtype=torch.uint8, device=dev)
+        vd = torch.empty_like(kd)
+    else:
+        kd = torch.from_numpy(synthetic.to_f16_bits(k)).view(torch.float16).to(dev)
+        vd = torch.from_numpy(synthetic.to_f16_bits(v)).view(torch.float16).to(dev)
+    row = q8a.ROW_BYTES[kv_dtype]
+    m, l, o = q8a.alloc_state(w.B, w.H, w.M, dev)
+    out = torch.empty((w.B, w.H, w.M, w.D), dtype=torch.float16, device=dev)
+    lse = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev)
+    chunks = [(s, min(chunk, w.N - s)) for s in range(0, w.N, chunk)]
+    acc_flops = [chunk_flops(w, s, n) for s, n in chunks]
+    n_rows = w.B * w.H * w.N
+
+    ev = {"pack": [], "init": [], "accumulate": [], "finalize": []}
+
+    def timed(name, fn, record):
+        if record:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[name].append((a, b))
+        else:
+            fn()
+
+    def step(record):
+        if kv_dtype == q8a.KV_Q8_0:
+            timed("pack", lambda: q8a.q8_0_pack(kx, kd, n_rows, 64), record)
+            timed("pack", lambda: q8a.q8_0_pack(vx, vd, n_rows, 64), record)
+        st = [None]
+
+        def init():
+            st[0] = q8a.attn_state_init(m, l, o, w.B, w.H, w.M, w.D, w.q_pos0)
+        timed("init", init, record)
+        kp, vp = kd.data_ptr(), vd.data_ptr()
+        for s, n in chunks:
+            timed("accumulate",
+                  lambda s=s, n=n: q8a.attn_accumulate_chunk(
+                      st[0], qd, kp + s * row, vp + s * row, kv_dtype, s, n, w.N * row,
+                      w.H * w.N * row, 1), record)
+        timed("finalize", lambda: q8a.attn_finalize(st[0], out, lse), record)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # clean timing of the step
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(False)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_clean = t0.elapsed_time(t1) / steps
+    # timed region with per-launch events (the roofline numbers come from here)
+    for key in ev:
+        ev[key].clear()
+    t0.record()
+    for _ in range(steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_events = t0.elapsed_time(t1) / steps
+    kern = {}
+    for key, pairs in ev.items():
+        if pairs:
+            d = [a.elapsed_time(b) for a, b in pairs]
+            kern[key] = {"launches_per_step": len(d) // steps, "mean_us": 1e3 * float(np.mean(d))}
+    acc_ms = [a.elapsed_time(b) for a, b in ev["accumulate"]]
+    acc_mean_ms = float(np.mean(acc_ms))
+    acc_flops_mean = float(np.mean(acc_flops))
+    res = dict(q=q, out=out, lse=lse, ms_clean=ms_clean, ms_events=ms_events, kernels=kern,
+               acc_mean_ms=acc_mean_ms, acc_flops_mean=acc_flops_mean,
+               acc_per_chunk_us=[1e3 * float(np.mean(acc_ms[i::len(chunks)]))
+                                 for i in range(len(chunks))],
+               acc_flops=acc_flops, k=k, v=v, chunks=chunks)
+    return res
+
+
+def cpu_baseline(w, res, kv_dtype, budget_s):
+    """The oracle on whole heads (b, h) in order until ~budget_s of wall time has passed."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    threads = oracle.default_threads()
+    q, k, v = res["q"], res["k"], res["v"]
+    out = res["out"].float().cpu().numpy().reshape(w.B * w.H, w.M, w.D)
+    lse = res["lse"].cpu().numpy().reshape(w.B * w.H, w.M)
+    pos = w.q_pos0 + np.arange(w.M, dtype=np.int64)
+    head_flops = int(np.minimum(pos + 1, w.N).sum()) * 4 * w.D
+    done = 0
+    err = []
+    t0 = time.perf_counter()
+    while done < w.B * w.H:
+        b, h = divmod(done, w.H)
+        qh = np.ascontiguousarray(q[b:b + 1, h:h + 1])
+        if kv_dtype == 0:
+            kb = oracle.q8_0_pack(k[b:b + 1, h:h + 1], threads)
+            vb = oracle.q8_0_pack(v[b:b + 1, h:h + 1], threads)
+            prob = oracle.Problem(qh, kb, vb, oracle.KV_Q8_0, w.q_pos0)
+        else:
+            kb = synthetic.to_f16_bits(k[b:b + 1, h:h + 1])
+            vb = synthetic.to_f16_bits(v[b:b + 1, h:h + 1])
+            prob = oracle.Problem(qh, kb, vb, oracle.KV_F16, w.q_pos0)
+        O_ref, lse_ref = oracle.attention(prob, nthreads=threads)
+        err.append((out[done].astype(np.float64) - O_ref, O_ref,
+                    lse[done].astype(np.float64) - lse_ref, lse_ref))
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    d = np.concatenate([e[0].ravel() for e in err])
+    r = np.concatenate([e[1].ravel() for e in err])
+    dl = np.concatenate([e[2] for e in err])
+    rl = np.concatenate([e[3] for e in err])
+    parity = {"heads_checked": done, "max_abs": float(np.abs(d).max()),
+              "rel_rms": float(np.sqrt((d ** 2).sum() / (r ** 2).sum())),
+              "lse_rel": float((np.abs(dl) / np.maximum(1, np.abs(rl))).max())}
+    parity["ok"] = parity["max_abs"] <= 2e-3 and parity["rel_rms"] <= 1e-3 and \
+        parity["lse_rel"] <= 1e-4
+    base = {"value": head_flops * done / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d (sequence, head) pairs in full (Q8_0 pack of their K and V + "
+                      "FP64 single-pass causal attention over all %d rows), %.1f s" % (
+                          done, w.B * w.H, w.M, dt)}
+    return base, parity
+
+
+def traffic_per_launch():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(t["hbm_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="0-3: resident workloads")
+    ap.add_argument("--chunk", type=int, default=None, help="override B_C")
+    ap.add_argument("--kv", choices=["q8_0", "f16"], default="q8_0")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path is single-GPU by design (no collectives "
+              "or sharding are built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import synthetic
+    import chunked_flashattention_q8_amd as q8a
+
+    w = synthetic.WORKLOADS[args.workload]
+    if w.streamed:
+        raise SystemExit("the streamed workload is measured by its own mode (not built here)")
+    kv_dtype = q8a.KV_Q8_0 if args.kv == "q8_0" else q8a.KV_F16
+    chunk = args.chunk or w.chunk
+    res = run_resident(w, kv_dtype, chunk, args.steps, args.warmup)
+
+    flops_step = w.visible_pairs() * 4 * w.D
+    ms = res["ms_events"]
+    value = flops_step / (ms * 1e-3) / 1e12
+    acc_achieved = res["acc_flops_mean"] / (res["acc_mean_ms"] * 1e-3) / 1e12
+    kv_bytes = 2 * w.B * w.H * w.N * q8a.ROW_BYTES[kv_dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: B=%d H=%d M=%d N=%d d=64 causal q_pos0=%d, %s KV, B_C=%d "
+                        "(%d chunk calls); step = pack K,V + init + chunk calls + finalize"
+                        % (w.name, w.B, w.H, w.M, w.N, w.q_pos0, args.kv.upper(), chunk,
+                           len(res["chunks"])),
+            "kv_dtype": args.kv, "chunk_tokens": chunk,
+        },
+        "roofline": {
+            "kernel": "accumulate_kernel",
+            "bound": "mfma",
+            "achieved": round(acc_achieved, 3),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(acc_achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic_per_launch() if (args.workload == 2 and chunk == 512 and
+                                                kv_dtype == q8a.KV_Q8_0) else None,
+            "flops_per_launch": res["acc_flops_mean"],
+            "mean_launch_us": round(1e3 * res["acc_mean_ms"], 3),
+        },
+        "step_fraction_of_mfma_peak": round(value / PEAK_F16_TFLOPS, 4),
+        "kv_gbps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "ms_per_step_without_kernel_events": round(res["ms_clean"], 5),
+        "kernels": res["kernels"],
+        "accumulate_us_per_chunk": [round(x, 3) for x in res["acc_per_chunk_us"]],
+    }
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(w, res, kv_dtype, args.cpu_seconds)
+        line["cpu_baseline"] = base
+        line["parity_vs_oracle"] = parity
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
