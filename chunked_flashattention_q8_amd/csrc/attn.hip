@@ -40,8 +40,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int QT = 128;  // query rows per workgroup
-constexpr int WQ = 32;   // query rows per wavefront
+constexpr int QT = 256;  // query rows per workgroup (4 wavefronts x 2 blocks of 32)
+constexpr int WQ = 32;   // query rows per MFMA block
 constexpr int KT = 64;   // keys per LDS tile
 constexpr int NTHR = 256;
 constexpr int KP = 72;   // LDS pitch (halves) of the K tiles (144-byte rows)
@@ -100,26 +100,149 @@ __device__ __forceinline__ half8 to_half8(const floatx16 &s, int base)
 }
 
 template <int FMT> // 0: Q8_0 rows (68 bytes), 1: FP16 rows (128 bytes)
-__global__ __launch_bounds__(NTHR) void accumulate_kernel(AccumulateArgs a)
+struct KvTile {     // one LDS buffer of unpacked MFMA operands for KT keys
+    _Float16 khi[KT * KP];                     // K (Q8_0: fp16(q*d)), [key][dim]
+    _Float16 klo[FMT == 0 ? KT * KP : 8];      // Q8_0: q*d - khi, [key][dim]
+    _Float16 vt[64 * VP];                      // V int8 values (Q8_0) or V (FP16), [dim][vpos]
+    _Float16 vsc[FMT == 0 ? 2 * KT : 8];       // Q8_0 V scales, [block][vpos]
+};
+
+template <int FMT>
+struct Smem {
+    static constexpr int ROW = FMT == 0 ? kQ8RowBytes : kF16RowBytes;
+    uint8_t raw[2][2][KT * ROW]; // [buffer][K, V][raw rows of KT keys]
+    KvTile<FMT> tile[2];
+};
+
+// Unpack the raw rows of one KV tile (LDS) into MFMA operand layout (LDS).  All 256 threads.
+template <int FMT>
+__device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
+                                            const uint8_t *__restrict__ rv, KvTile<FMT> &T,
+                                            int tid)
 {
-    constexpr int ROW = FMT == 0 ? kQ8RowBytes : kF16RowBytes;
-    constexpr int RAW = KT * ROW;
-    constexpr int RAW16 = RAW / 16;
-    __shared__ __align__(16) uint8_t raw[2][RAW];
-    __shared__ __align__(16) _Float16 khi[KT * KP];
-    __shared__ __align__(16) _Float16 klo[FMT == 0 ? KT * KP : 8];
-    __shared__ __align__(16) _Float16 vt[64 * VP];
-    __shared__ __align__(16) _Float16 vsc[FMT == 0 ? 2 * KT : 8];
+    if constexpr (FMT == 0) {
+        { // K: thread = (block, key, 16-value half); waves 0-1 block 0, waves 2-3 block 1
+            const int blk = tid >> 7, key = (tid & 127) >> 1, hh = tid & 1;
+            const uint8_t *rr = rk + key * 68;
+            uint32_t w[4];
+            if (blk == 0) { // values at byte 2 + 16*hh: realign by 2 bytes
+                const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 16 * hh);
+                const uint32_t x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3], x4 = p[4];
+                w[0] = __builtin_amdgcn_alignbyte(x1, x0, 2);
+                w[1] = __builtin_amdgcn_alignbyte(x2, x1, 2);
+                w[2] = __builtin_amdgcn_alignbyte(x3, x2, 2);
+                w[3] = __builtin_amdgcn_alignbyte(x4, x3, 2);
+            } else {        // values at byte 36 + 16*hh: dword aligned
+                const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 36 + 16 * hh);
+                w[0] = p[0]; w[1] = p[1]; w[2] = p[2]; w[3] = p[3];
+            }
+            const _Float16 d = *reinterpret_cast<const _Float16 *>(rr + 34 * blk);
+            const half2v d2 = {d, d};
+            half8 hi8[2], lo8[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                half2v q01, q23;
+                i8x4_to_f16(w[i], q01, q23);
+                const half2v h01 = q01 * d2, h23 = q23 * d2;
+                const half2v l01 = __builtin_elementwise_fma(q01, d2, -h01);
+                const half2v l23 = __builtin_elementwise_fma(q23, d2, -h23);
+                hi8[i >> 1][4 * (i & 1) + 0] = h01[0]; hi8[i >> 1][4 * (i & 1) + 1] = h01[1];
+                hi8[i >> 1][4 * (i & 1) + 2] = h23[0]; hi8[i >> 1][4 * (i & 1) + 3] = h23[1];
+                lo8[i >> 1][4 * (i & 1) + 0] = l01[0]; lo8[i >> 1][4 * (i & 1) + 1] = l01[1];
+                lo8[i >> 1][4 * (i & 1) + 2] = l23[0]; lo8[i >> 1][4 * (i & 1) + 3] = l23[1];
+            }
+            half8 *dh = reinterpret_cast<half8 *>(&T.khi[key * KP + 32 * blk + 16 * hh]);
+            half8 *dl = reinterpret_cast<half8 *>(&T.klo[key * KP + 32 * blk + 16 * hh]);
+            dh[0] = hi8[0]; dh[1] = hi8[1];
+            dl[0] = lo8[0]; dl[1] = lo8[1];
+        }
+        { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
+            const int kq = tid & 15, dg = tid >> 4, blk = dg >> 3;
+            uint32_t x[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint8_t *rr = rv + (4 * kq + c) * 68;
+                if (blk == 0) {
+                    const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 4 * dg);
+                    x[c] = __builtin_amdgcn_alignbyte(p[1], p[0], 2);
+                } else {
+                    x[c] = *reinterpret_cast<const uint32_t *>(rr + 36 + 4 * (dg - 8));
+                }
+            }
+            const int p0 = vpos(4 * kq);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t y = byte_of(x[0], d) | (byte_of(x[1], d) << 8) |
+                                   (byte_of(x[2], d) << 16) | (byte_of(x[3], d) << 24);
+                half2v lo, hi;
+                i8x4_to_f16(y, lo, hi);
+                const half4 r4 = {lo[0], lo[1], hi[0], hi[1]};
+                *reinterpret_cast<half4 *>(&T.vt[(4 * dg + d) * VP + p0]) = r4;
+            }
+            if (tid < 2 * KT) {
+                const int key = tid & 63, sb = tid >> 6;
+                T.vsc[sb * KT + vpos(key)] =
+                    *reinterpret_cast<const _Float16 *>(rv + key * 68 + 34 * sb);
+            }
+        }
+    } else {
+        { // K: straight copy into the padded tile
+            const int key = tid >> 2, qq = tid & 3;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(rk + key * 128 + 32 * qq);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(&T.khi[key * KP + 16 * qq]);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
+        { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
+            const int kq = tid & 15, dg = tid >> 4;
+            half4 x[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                x[c] = *reinterpret_cast<const half4 *>(rv + (4 * kq + c) * 128 + 8 * dg);
+            const int p0 = vpos(4 * kq);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const half4 r4 = {x[0][d], x[1][d], x[2][d], x[3][d]};
+                *reinterpret_cast<half4 *>(&T.vt[(4 * dg + d) * VP + p0]) = r4;
+            }
+        }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
+{
+    constexpr int ROW = Smem<FMT>::ROW;
+    constexpr int RAW16 = KT * ROW / 16;                 // 16-byte pieces per tensor tile
+    constexpr int NPRE = FMT == 0 ? 3 : 4;               // prefetch slots per thread
+    static_assert(FMT != 0 || (RAW16 > NTHR && RAW16 - NTHR <= 64), "slot layout");
+    static_assert(FMT == 0 || RAW16 == 2 * NTHR, "slot layout");
+    __shared__ Smem<FMT> sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int qcol = lane & 31, g = lane >> 5;
-    const int qt = (int)gridDim.x - 1 - (int)blockIdx.x; // tiles with more visible keys first
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int64_t head = (int64_t)b * a.H + h;
 
-    // keys [0, end) of the chunk are visible to query row qrow
-    auto kv_end_for = [&](int qrow) -> int {
+    // ---- workgroup -> (sequence, head, query tile).  Workgroups are dispatched round-robin over
+    // the 8 XCDs; each XCD gets a contiguous set of heads (their K/V stay in its L2) and within
+    // it the query tiles that see the most keys come first.
+    const int n_qt = (a.M + QT - 1) / QT;
+    const int BH = a.B * a.H;
+    const int wg = blockIdx.x;
+    int r, head_i;
+    if (BH % 8 == 0) {
+        const int hpx = BH / 8, slot = wg / 8;
+        r = slot / hpx;
+        head_i = (wg % 8) * hpx + slot % hpx;
+    } else {
+        r = wg / BH;
+        head_i = wg % BH;
+    }
+    const int qt = n_qt - 1 - r;
+    const int b = head_i / a.H, h = head_i % a.H;
+    const int64_t head = head_i;
+
+    auto kv_end_for = [&](int qrow) -> int { // keys [0, end) of the chunk visible to query qrow
         if (!a.causal)
             return a.n_kv;
         const int64_t e = a.q_pos0 + qrow - a.kv_pos0 + 1;
@@ -131,262 +254,269 @@ __global__ __launch_bounds__(NTHR) void accumulate_kernel(AccumulateArgs a)
         return; // the whole workgroup sees nothing of this chunk
     const int n_tiles = (kv_end_wg + KT - 1) / KT;
 
-    const int q_w0 = q_wg0 + wave * WQ;
-    const bool wave_live = q_w0 < a.M;
-    const bool wave_full = q_w0 + WQ <= a.M;
-    const int kv_end_w = wave_live ? kv_end_for(min(q_w0 + WQ, a.M) - 1) : 0;
-    const int kv_full_w = wave_full ? kv_end_for(q_w0) : 0; // visible to every row of the wave
-    const bool active = kv_end_w > 0;
-
-    const int qi = q_w0 + qcol;
-    const bool q_ok = qi < a.M;
-    const int64_t qpos = a.q_pos0 + qi;
-    const int64_t row = head * a.M + qi;
-
-    half8 qreg[4];
-    floatx16 o0, o1;
+    // ---- this wavefront's two 32-row query blocks: w and 7 - w of the tile (balances the
+    // causal diagonal across wavefronts)
+    int kv_end_b[2], kv_full_b[2], qi[2];
+    bool q_ok[2];
+    int64_t qpos[2], row[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        o0[v] = 0.f;
-        o1[v] = 0.f;
+    for (int j = 0; j < 2; ++j) {
+        const int q0 = q_wg0 + WQ * (j == 0 ? wave : 7 - wave);
+        const bool live = q0 < a.M;
+        kv_end_b[j] = live ? kv_end_for(min(q0 + WQ, a.M) - 1) : 0;
+        kv_full_b[j] = (q0 + WQ <= a.M) ? kv_end_for(q0) : 0;
+        qi[j] = q0 + qcol;
+        q_ok[j] = qi[j] < a.M;
+        qpos[j] = a.q_pos0 + qi[j];
+        row[j] = head * a.M + qi[j];
     }
-    float l_part = 0.f;
-    float m_raw = -INFINITY; // running max of the raw dot products Q.K (scaled logit * 8)
-    float m_ref = -INFINITY; // reference maximum of the exponentials, log2 units
-    bool saw = false;
-    if (active && q_ok) {
-        const half8 *qrow = reinterpret_cast<const half8 *>(
-            reinterpret_cast<const _Float16 *>(a.q) + row * kHeadDim);
+    const int kv_end_w = max(kv_end_b[0], kv_end_b[1]);
+
+    half8 qreg[2][4];
+    floatx16 o[2][2];
+    float l_part[2], m_raw[2], m_ref[2];
+    bool saw[2];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qreg[kk] = qrow[2 * kk + g];
-        const float mo = a.m[row];
-        if (mo != -INFINITY) {
-            m_raw = mo * 8.0f;
-            m_ref = m_raw * kScaleLog2;
-            if (g == 0)
-                l_part = a.l[row];
-            const float4 *orow = reinterpret_cast<const float4 *>(a.o + row * kHeadDim);
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 x = orow[2 * k + g];
-                const float4 y = orow[8 + 2 * k + g];
-                o0[4 * k + 0] = x.x; o0[4 * k + 1] = x.y; o0[4 * k + 2] = x.z; o0[4 * k + 3] = x.w;
-                o1[4 * k + 0] = y.x; o1[4 * k + 1] = y.y; o1[4 * k + 2] = y.z; o1[4 * k + 3] = y.w;
-            }
+        for (int v = 0; v < 16; ++v) {
+            o[j][0][v] = 0.f;
+            o[j][1][v] = 0.f;
         }
-    } else {
+        l_part[j] = 0.f;
+        m_raw[j] = -INFINITY; // running max of the raw dot products Q.K (= scaled logit * 8)
+        m_ref[j] = -INFINITY; // reference maximum of the exponentials, log2 units
+        saw[j] = false;
+        if (kv_end_b[j] > 0 && q_ok[j]) {
+            const half8 *qrow = reinterpret_cast<const half8 *>(
+                reinterpret_cast<const _Float16 *>(a.q) + row[j] * kHeadDim);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qreg[kk] = half8{};
+            for (int kk = 0; kk < 4; ++kk)
+                qreg[j][kk] = qrow[2 * kk + g];
+            const float mo = a.m[row[j]];
+            if (mo != -INFINITY) { // non-empty row: resume from its state
+                m_raw[j] = mo * 8.0f;
+                m_ref[j] = m_raw[j] * kScaleLog2;
+                if (g == 0)
+                    l_part[j] = a.l[row[j]];
+                const float4 *orow = reinterpret_cast<const float4 *>(a.o + row[j] * kHeadDim);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float4 x = orow[2 * k + g];
+                    const float4 y = orow[8 + 2 * k + g];
+                    o[j][0][4 * k + 0] = x.x; o[j][0][4 * k + 1] = x.y;
+                    o[j][0][4 * k + 2] = x.z; o[j][0][4 * k + 3] = x.w;
+                    o[j][1][4 * k + 0] = y.x; o[j][1][4 * k + 1] = y.y;
+                    o[j][1][4 * k + 2] = y.z; o[j][1][4 * k + 3] = y.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qreg[j][kk] = half8{};
+        }
     }
 
+    // ---- K/V tile pipeline: raw rows of tile t+2 are fetched into registers while tile t is
+    // computed and tile t+1 is unpacked; one barrier per tile.
     const uint8_t *kbase = a.k + b * a.kv_seq_stride + h * a.kv_head_stride;
     const uint8_t *vbase = a.v + b * a.kv_seq_stride + h * a.kv_head_stride;
     const uint32_t head_bytes = (uint32_t)a.n_kv * ROW;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, head_bytes);
+    // Prefetch slots: each slot is one 16-byte piece of the K or the V tile, and within a
+    // wavefront a slot always belongs to the same tensor (buffer resources must be uniform).
+    //   Q8_0 (272 pieces per tensor): slot 0 = K piece tid, slot 1 = V piece tid, slot 2 = the
+    //   16 remaining K pieces on wavefront 0 and the 16 remaining V pieces on wavefront 1.
+    //   FP16 (512 pieces per tensor): slots 0, 1 = K pieces tid, tid + 256; slots 2, 3 = V.
+    u32x4 pre[NPRE];
+    auto slot = [&](int sl, int &tensor, int &piece) -> bool {
+        if constexpr (FMT == 0) {
+            if (sl < 2) {
+                tensor = sl;
+                piece = tid;
+                return true;
+            }
+            tensor = wave;
+            piece = NTHR + lane;
+            return wave < 2 && lane < RAW16 - NTHR;
+        } else {
+            tensor = sl >> 1;
+            piece = tid + NTHR * (sl & 1);
+            return true;
+        }
+    };
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int sl = 0; sl < NPRE; ++sl) {
+            int tensor, piece;
+            if (slot(sl, tensor, piece)) {
+                const uint32_t off = (uint32_t)t * (KT * ROW) + 16u * piece;
+                pre[sl] = load16(tensor ? rv : rk, off, head_bytes);
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int sl = 0; sl < NPRE; ++sl) {
+            int tensor, piece;
+            if (slot(sl, tensor, piece))
+                *reinterpret_cast<u32x4 *>(&sm.raw[buf][tensor][16 * piece]) = pre[sl];
+        }
+    };
+
+    fetch(0);
+    stash(0);
+    if (n_tiles > 1) {
+        fetch(1);
+        stash(1);
+    }
+    __syncthreads();
+    unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid);
+    __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
+        if (t + 2 < n_tiles)
+            fetch(t + 2);
+        const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
-        // ---- 1. raw K and V rows of keys [key0, key0 + 64) -> LDS (coalesced 128-bit loads)
-        for (int i = tid; i < RAW16; i += NTHR) {
-            const uint32_t off = (uint32_t)key0 * ROW + 16u * i;
-            *reinterpret_cast<u32x4 *>(&raw[0][16 * i]) = load16(rk, off, head_bytes);
-            *reinterpret_cast<u32x4 *>(&raw[1][16 * i]) = load16(rv, off, head_bytes);
-        }
-        __syncthreads();
-
-        // ---- 2. unpack into the MFMA operand tiles
-        if constexpr (FMT == 0) {
-            { // K: thread = (block, key, 16-value half of the block); waves 0-1 block 0, 2-3 block 1
-                const int blk = tid >> 7, key = (tid & 127) >> 1, hh = tid & 1;
-                const uint8_t *rr = &raw[0][key * 68];
-                uint32_t w[4];
-                if (blk == 0) { // values at byte 2 + 16*hh: realign by 2 bytes
-                    const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 16 * hh);
-                    const uint32_t x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3], x4 = p[4];
-                    w[0] = __builtin_amdgcn_alignbyte(x1, x0, 2);
-                    w[1] = __builtin_amdgcn_alignbyte(x2, x1, 2);
-                    w[2] = __builtin_amdgcn_alignbyte(x3, x2, 2);
-                    w[3] = __builtin_amdgcn_alignbyte(x4, x3, 2);
-                } else {        // values at byte 36 + 16*hh: dword aligned
-                    const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 36 + 16 * hh);
-                    w[0] = p[0]; w[1] = p[1]; w[2] = p[2]; w[3] = p[3];
-                }
-                const _Float16 d = *reinterpret_cast<const _Float16 *>(rr + 34 * blk);
-                const half2v d2 = {d, d};
-                half8 hi8[2], lo8[2];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    half2v q01, q23;
-                    i8x4_to_f16(w[i], q01, q23);
-                    const half2v h01 = q01 * d2, h23 = q23 * d2;
-                    const half2v l01 = __builtin_elementwise_fma(q01, d2, -h01);
-                    const half2v l23 = __builtin_elementwise_fma(q23, d2, -h23);
-                    hi8[i >> 1][4 * (i & 1) + 0] = h01[0]; hi8[i >> 1][4 * (i & 1) + 1] = h01[1];
-                    hi8[i >> 1][4 * (i & 1) + 2] = h23[0]; hi8[i >> 1][4 * (i & 1) + 3] = h23[1];
-                    lo8[i >> 1][4 * (i & 1) + 0] = l01[0]; lo8[i >> 1][4 * (i & 1) + 1] = l01[1];
-                    lo8[i >> 1][4 * (i & 1) + 2] = l23[0]; lo8[i >> 1][4 * (i & 1) + 3] = l23[1];
-                }
-                half8 *dh = reinterpret_cast<half8 *>(&khi[key * KP + 32 * blk + 16 * hh]);
-                half8 *dl = reinterpret_cast<half8 *>(&klo[key * KP + 32 * blk + 16 * hh]);
-                dh[0] = hi8[0]; dh[1] = hi8[1];
-                dl[0] = lo8[0]; dl[1] = lo8[1];
-            }
-            { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
-                const int kq = tid & 15, dg = tid >> 4, blk = dg >> 3;
-                uint32_t x[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint8_t *rr = &raw[1][(4 * kq + c) * 68];
-                    if (blk == 0) {
-                        const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 4 * dg);
-                        x[c] = __builtin_amdgcn_alignbyte(p[1], p[0], 2);
-                    } else {
-                        x[c] = *reinterpret_cast<const uint32_t *>(rr + 36 + 4 * (dg - 8));
-                    }
-                }
-                const int p0 = vpos(4 * kq);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t y = byte_of(x[0], d) | (byte_of(x[1], d) << 8) |
-                                       (byte_of(x[2], d) << 16) | (byte_of(x[3], d) << 24);
-                    half2v lo, hi;
-                    i8x4_to_f16(y, lo, hi);
-                    const half4 r4 = {lo[0], lo[1], hi[0], hi[1]};
-                    *reinterpret_cast<half4 *>(&vt[(4 * dg + d) * VP + p0]) = r4;
-                }
-                if (tid < 2 * KT) {
-                    const int key = tid & 63, sb = tid >> 6;
-                    vsc[sb * KT + vpos(key)] =
-                        *reinterpret_cast<const _Float16 *>(&raw[1][key * 68 + 34 * sb]);
-                }
-            }
-        } else {
-            { // K: straight copy into the padded tile
-                const int key = tid >> 2, qq = tid & 3;
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(&raw[0][key * 128 + 32 * qq]);
-                u32x4 *dst = reinterpret_cast<u32x4 *>(&khi[key * KP + 16 * qq]);
-                dst[0] = src[0];
-                dst[1] = src[1];
-            }
-            { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
-                const int kq = tid & 15, dg = tid >> 4;
-                half4 x[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    x[c] = *reinterpret_cast<const half4 *>(&raw[1][(4 * kq + c) * 128 + 8 * dg]);
-                const int p0 = vpos(4 * kq);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const half4 r4 = {x[0][d], x[1][d], x[2][d], x[3][d]};
-                    *reinterpret_cast<half4 *>(&vt[(4 * dg + d) * VP + p0]) = r4;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- 3. this wavefront's 32 query rows against the 64 keys of the tile
         if (key0 < kv_end_w) {
-            floatx16 s[2];
+            // S^T = K Q^T for both query blocks: lane (qcol, g) holds
+            // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][sub][v]
+            floatx16 s[2][2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        s[j][sub][v] = 0.f;
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
-                floatx16 acc;
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[v] = 0.f;
                 const int kr = (32 * sub + qcol) * KP + 8 * g;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const half8 ah = *reinterpret_cast<const half8 *>(&khi[kr + 16 * kk]);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[kk], acc, 0, 0, 0);
+                    const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[j][kk],
+                                                                          s[j][sub], 0, 0, 0);
                     if constexpr (FMT == 0) {
-                        const half8 al = *reinterpret_cast<const half8 *>(&klo[kr + 16 * kk]);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qreg[kk], acc, 0, 0, 0);
+                        const half8 al = *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                al, qreg[j][kk], s[j][sub], 0, 0, 0);
                     }
                 }
-                s[sub] = acc;
             }
-            // lane (qcol, g) holds S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol]
-            if (key0 + KT > kv_full_w) {
+            bool need_any = false;
+            float mx2[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (key0 + KT > kv_full_b[j]) { // causal diagonal, ragged tail or padding rows
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int kc = key0 + 32 * sub + 8 * (v >> 2) + 4 * g + (v & 3);
+                            const bool ok = q_ok[j] && kc < a.n_kv &&
+                                            (!a.causal || a.kv_pos0 + kc <= qpos[j]);
+                            s[j][sub][v] = ok ? s[j][sub][v] : -INFINITY;
+                        }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    mx = fmaxf(mx, fmaxf(s[j][0][v], s[j][1][v]));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                m_raw[j] = fmaxf(m_raw[j], mx);
+                saw[j] = saw[j] || (mx != -INFINITY);
+                mx2[j] = mx * kScaleLog2;
+                need_any = need_any || (mx2[j] > m_ref[j] + kTau);
+            }
+            if (__builtin_amdgcn_ballot_w64(need_any)) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
+                    const float alpha =
+                        (m_ref[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
+                    l_part[j] *= alpha;
+                    o[j][0] *= alpha;
+                    o[j][1] *= alpha;
+                    m_ref[j] = m_new;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
+                float lsum = 0.f;
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int kc = key0 + 32 * sub + 8 * (v >> 2) + 4 * g + (v & 3);
-                        const bool ok = q_ok && kc < a.n_kv &&
-                                        (!a.causal || a.kv_pos0 + kc <= qpos);
-                        s[sub][v] = ok ? s[sub][v] : -INFINITY;
+                        const float p = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(s[j][sub][v], kScaleLog2, -base));
+                        s[j][sub][v] = p;
+                        lsum += p;
                     }
+                l_part[j] += lsum;
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                mx = fmaxf(mx, fmaxf(s[0][v], s[1][v]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            m_raw = fmaxf(m_raw, mx);
-            saw = saw || (mx != -INFINITY);
-            const float mx2 = mx * kScaleLog2;
-            const bool need = mx2 > m_ref + kTau;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                const float m_new = need ? mx2 : m_ref;
-                const float alpha =
-                    (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                l_part *= alpha;
-                o0 *= alpha;
-                o1 *= alpha;
-                m_ref = m_new;
-            }
-            const float base = (m_ref == -INFINITY) ? 0.f : m_ref;
-            float lsum = 0.f;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][v], kScaleLog2, -base));
-                    s[sub][v] = p;
-                    lsum += p;
-                }
-            l_part += lsum;
+            // O^T += V^T P^T; the V tile's key order matches the accumulator layout
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const half8 p16 = to_half8(s[sub], 8 * tt);
                     const int pos = 32 * sub + 16 * tt + 8 * g;
-                    half8 b0, b1;
+                    const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
+                    const half8 a1 =
+                        *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
+                    half8 sc0, sc1;
                     if constexpr (FMT == 0) {
-                        b0 = p16 * *reinterpret_cast<const half8 *>(&vsc[pos]);
-                        b1 = p16 * *reinterpret_cast<const half8 *>(&vsc[KT + pos]);
-                    } else {
-                        b0 = p16;
-                        b1 = p16;
+                        sc0 = *reinterpret_cast<const half8 *>(&T.vsc[pos]);
+                        sc1 = *reinterpret_cast<const half8 *>(&T.vsc[KT + pos]);
                     }
-                    const half8 a0 = *reinterpret_cast<const half8 *>(&vt[qcol * VP + pos]);
-                    const half8 a1 = *reinterpret_cast<const half8 *>(&vt[(32 + qcol) * VP + pos]);
-                    o0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, o0, 0, 0, 0);
-                    o1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, o1, 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const half8 p16 = to_half8(s[j][sub], 8 * tt);
+                        half8 b0 = p16, b1 = p16;
+                        if constexpr (FMT == 0) {
+                            b0 = p16 * sc0;
+                            b1 = p16 * sc1;
+                        }
+                        o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, o[j][0], 0, 0, 0);
+                        o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, o[j][1], 0, 0, 0);
+                    }
                 }
         }
+        if (t + 1 < n_tiles)
+            unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
+                             sm.tile[(t + 1) & 1], tid);
+        if (t + 2 < n_tiles)
+            stash(t & 1);
+        __syncthreads();
     }
 
     // ---- write back the rows that saw at least one key, renormalised to the true maximum
-    if (active) {
-        const float l_tot = l_part + __shfl_xor(l_part, 32);
-        if (q_ok && saw) {
-            const float r = __builtin_amdgcn_exp2f(m_ref - m_raw * kScaleLog2);
-            float4 *orow = reinterpret_cast<float4 *>(a.o + row * kHeadDim);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                orow[2 * k + g] = make_float4(o0[4 * k] * r, o0[4 * k + 1] * r,
-                                              o0[4 * k + 2] * r, o0[4 * k + 3] * r);
-                orow[8 + 2 * k + g] = make_float4(o1[4 * k] * r, o1[4 * k + 1] * r,
-                                                  o1[4 * k + 2] * r, o1[4 * k + 3] * r);
-            }
-            if (g == 0) {
-                a.m[row] = m_raw * 0.125f;
-                a.l[row] = l_tot * r;
+    for (int j = 0; j < 2; ++j) {
+        if (kv_end_b[j] > 0) { // uniform per wavefront
+            const float l_tot = l_part[j] + __shfl_xor(l_part[j], 32);
+            if (q_ok[j] && saw[j]) {
+                const float rr = __builtin_amdgcn_exp2f(m_ref[j] - m_raw[j] * kScaleLog2);
+                float4 *orow = reinterpret_cast<float4 *>(a.o + row[j] * kHeadDim);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    orow[2 * k + g] = make_float4(o[j][0][4 * k] * rr, o[j][0][4 * k + 1] * rr,
+                                                  o[j][0][4 * k + 2] * rr, o[j][0][4 * k + 3] * rr);
+                    orow[8 + 2 * k + g] =
+                        make_float4(o[j][1][4 * k] * rr, o[j][1][4 * k + 1] * rr,
+                                    o[j][1][4 * k + 2] * rr, o[j][1][4 * k + 3] * rr);
+                }
+                if (g == 0) {
+                    a.m[row[j]] = m_raw[j] * 0.125f;
+                    a.l[row[j]] = l_tot * rr;
+                }
             }
         }
     }
@@ -446,7 +576,7 @@ hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s)
 
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s)
 {
-    const dim3 grid((unsigned)((a.M + QT - 1) / QT), (unsigned)a.H, (unsigned)a.B);
+    const dim3 grid((unsigned)(((a.M + QT - 1) / QT) * a.B * a.H));
     if (kv_dtype == 0)
         hipLaunchKernelGGL(accumulate_kernel<0>, grid, dim3(NTHR), 0, s, a);
     else
