@@ -8,24 +8,28 @@
 // l' = l alpha + sum beta, O' = O alpha + sum beta_j V_j.  Keys and values are block_q8_0
 // ("Core Architecture & The 4-Brick Pipeline", Sec. 5).
 //
-// Accumulate kernel, one workgroup = 4 wavefronts = 128 query rows of one (sequence, head):
-//   * K/V tiles of 64 keys are fetched with 128-bit buffer loads (out-of-range bytes read as 0)
-//     into LDS as raw Q8_0 rows, then unpacked in LDS:
+// Accumulate kernel, one workgroup = 4 wavefronts = 256 query rows of one (sequence, head):
+//   * K/V tiles of 64 keys are fetched with 128-bit buffer loads (bytes past the chunk read as
+//     0) two tiles ahead into registers, staged in LDS as raw Q8_0 rows, then unpacked in LDS
+//     into a double-buffered operand tile (one barrier per tile):
 //       - K: the exact int8 values times the FP16 scale, split into two FP16 halves
 //         hi = fp16(q*d) and lo = q*d - hi (exact, q*d has at most 18 significant bits), so
 //         Q.K^T on FP16 MFMA reproduces the dequantised logits up to FP32 accumulation;
 //       - V: the exact int8 values as FP16, transposed to [dim][key]; its FP16 scales are kept
 //         per key and folded into the probabilities (P * d16, FP16) before the PV product.
-//   * Each wavefront owns 32 query rows and computes S^T = K Q^T with v_mfma_f32_32x32x16_f16,
-//     so each lane holds 16 logits of ONE query: the row max needs one cross-lane step and the
-//     rescale factor is per lane.  P stays in registers as the B operand of O^T += V^T P^T; the
-//     key order of the transposed V tile is permuted to match the accumulator layout.
+//   * Each wavefront owns two 32-row query blocks (w and 7 - w of the tile, which balances the
+//     causal diagonal) and computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so each lane
+//     holds 16 logits of ONE query per 32 keys: the row max needs one cross-lane step and the
+//     rescale factor is per lane.  P stays in registers as the B operand of O^T += V^T P^T;
+//     the key order of the transposed V tile is permuted to match the accumulator layout.
 //   * Softmax in base 2 with 1/sqrt(64)*log2(e) folded into one FMA.  The reference maximum is
 //     raised only when a tile's maximum exceeds it by more than 8 (log2 units), so O and l are
 //     rarely rescaled; the state written back is renormalised to the true running maximum.
 //   * Tiles wholly above the causal diagonal are skipped ("Core Architecture ...", Sec. 5,
 //     causal skipping); rows that see no key of the chunk are not written.
 //   * A state row whose m is -inf is empty: its O and l are not read.
+//   * Workgroups are ordered so that each XCD works on a contiguous set of heads (their K/V
+//     stay in that XCD's L2) and the query tiles that see the most keys start first.
 #include <hip/hip_fp16.h>
 
 #include "q8attn_internal.h"
@@ -54,19 +58,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
 }
 
-// 16 bytes at byte offset `off` of a buffer whose size is `bytes` (a multiple of 4).  Bytes past
-// the end read as zero; a 16-byte piece that straddles the end is fetched as four dwords so that
-// the in-range dwords are kept.
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t bytes)
+// 16 bytes at byte offset `off` of a buffer resource; bytes past its range read as zero.
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    if (off + 16u <= bytes || off >= bytes)
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    u32x4 x;
-    x[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    x[1] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0);
-    x[2] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8, 0, 0);
-    x[3] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 12, 0, 0);
-    return x;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // Four signed bytes -> four FP16 values (exact).  Each byte is biased to unsigned, placed in the
@@ -99,6 +94,28 @@ __device__ __forceinline__ half8 to_half8(const floatx16 &s, int base)
     return r;
 }
 
+__device__ __forceinline__ float vmax3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max(x[lane], x[lane ^ 32]): lanes l and l + 32 hold the same query row
+__device__ __forceinline__ float half_swap_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int FMT> // 0: Q8_0 rows (68 bytes), 1: FP16 rows (128 bytes)
 struct KvTile {     // one LDS buffer of unpacked MFMA operands for KT keys
     _Float16 khi[KT * KP];                     // K (Q8_0: fp16(q*d)), [key][dim]
@@ -118,7 +135,7 @@ struct Smem {
 template <int FMT>
 __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                                             const uint8_t *__restrict__ rv, KvTile<FMT> &T,
-                                            int tid)
+                                            int tid, int valid_keys)
 {
     if constexpr (FMT == 0) {
         { // K: thread = (block, key, 16-value half); waves 0-1 block 0, waves 2-3 block 1
@@ -179,10 +196,10 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                 const half4 r4 = {lo[0], lo[1], hi[0], hi[1]};
                 *reinterpret_cast<half4 *>(&T.vt[(4 * dg + d) * VP + p0]) = r4;
             }
-            if (tid < 2 * KT) {
+            if (tid < 2 * KT) { // keys past the chunk end get scale 0 (their P is 0 too)
                 const int key = tid & 63, sb = tid >> 6;
-                T.vsc[sb * KT + vpos(key)] =
-                    *reinterpret_cast<const _Float16 *>(rv + key * 68 + 34 * sb);
+                const _Float16 d = *reinterpret_cast<const _Float16 *>(rv + key * 68 + 34 * sb);
+                T.vsc[sb * KT + vpos(key)] = key < valid_keys ? d : (_Float16)0.0f;
             }
         }
     } else {
@@ -220,7 +237,8 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     __shared__ Smem<FMT> sm;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: keep it scalar
     const int qcol = lane & 31, g = lane >> 5;
 
     // ---- workgroup -> (sequence, head, query tile).  Workgroups are dispatched round-robin over
@@ -256,9 +274,9 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 
     // ---- this wavefront's two 32-row query blocks: w and 7 - w of the tile (balances the
     // causal diagonal across wavefronts)
-    int kv_end_b[2], kv_full_b[2], qi[2];
+    int kv_end_b[2], kv_full_b[2], qi[2], lim[2];
     bool q_ok[2];
-    int64_t qpos[2], row[2];
+    int64_t row[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int q0 = q_wg0 + WQ * (j == 0 ? wave : 7 - wave);
@@ -267,7 +285,8 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         kv_full_b[j] = (q0 + WQ <= a.M) ? kv_end_for(q0) : 0;
         qi[j] = q0 + qcol;
         q_ok[j] = qi[j] < a.M;
-        qpos[j] = a.q_pos0 + qi[j];
+        // last chunk key this lane's query sees (-1: none)
+        lim[j] = q_ok[j] ? kv_end_for(qi[j]) - 1 : -1;
         row[j] = head * a.M + qi[j];
     }
     const int kv_end_w = max(kv_end_b[0], kv_end_b[1]);
@@ -321,7 +340,10 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     // computed and tile t+1 is unpacked; one barrier per tile.
     const uint8_t *kbase = a.k + b * a.kv_seq_stride + h * a.kv_head_stride;
     const uint8_t *vbase = a.v + b * a.kv_seq_stride + h * a.kv_head_stride;
-    const uint32_t head_bytes = (uint32_t)a.n_kv * ROW;
+    // The range is rounded up to 16 bytes: the last 16-byte piece may hold up to 12 bytes past
+    // the chunk, never past the 16-byte-aligned block that ends it (so never into another page);
+    // those bytes belong to keys beyond n_kv, which are masked and get a zero V scale.
+    const uint32_t head_bytes = ((uint32_t)a.n_kv * ROW + 15u) & ~15u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, head_bytes);
     // Prefetch slots: each slot is one 16-byte piece of the K or the V tile, and within a
@@ -352,7 +374,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             int tensor, piece;
             if (slot(sl, tensor, piece)) {
                 const uint32_t off = (uint32_t)t * (KT * ROW) + 16u * piece;
-                pre[sl] = load16(tensor ? rv : rk, off, head_bytes);
+                pre[sl] = load16(tensor ? rv : rk, off);
             }
         }
     };
@@ -372,7 +394,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         stash(1);
     }
     __syncthreads();
-    unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid);
+    unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
     __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
@@ -381,117 +403,130 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
         if (key0 < kv_end_w) {
-            // S^T = K Q^T for both query blocks: lane (qcol, g) holds
-            // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][sub][v]
-            floatx16 s[2][2];
+            // One 64-key tile for both query blocks.  The 32-key subtiles that some row of a
+            // block cannot wholly see (causal diagonal, ragged chunk end, padding rows) are masked
+            // element by element; the others -- the common case -- are not touched.
+            {
+                // S^T = K Q^T: lane (qcol, g) holds
+                // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][sub][v]
+                floatx16 s[2][2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
+                    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        s[j][sub][v] = 0.f;
+                        for (int v = 0; v < 16; ++v)
+                            s[j][sub][v] = 0.f;
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                const int kr = (32 * sub + qcol) * KP + 8 * g;
+                for (int sub = 0; sub < 2; ++sub) {
+                    const int kr = (32 * sub + qcol) * KP + 8 * g;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[j][kk],
-                                                                          s[j][sub], 0, 0, 0);
-                    if constexpr (FMT == 0) {
-                        const half8 al = *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
                             s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                al, qreg[j][kk], s[j][sub], 0, 0, 0);
+                                ah, qreg[j][kk], s[j][sub], 0, 0, 0);
+                        if constexpr (FMT == 0) {
+                            const half8 al =
+                                *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
+#pragma unroll
+                            for (int j = 0; j < 2; ++j)
+                                s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    al, qreg[j][kk], s[j][sub], 0, 0, 0);
+                        }
                     }
                 }
-            }
-            bool need_any = false;
-            float mx2[2];
+                bool need_any = false;
+                float mx2[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (key0 + KT > kv_full_b[j]) { // causal diagonal, ragged tail or padding rows
+                for (int j = 0; j < 2; ++j) {
+                    {
+                        // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
+                        const int rel = lim[j] - key0 - 4 * g;
+#pragma unroll
+                        for (int sub = 0; sub < 2; ++sub)
+                            if (key0 + 32 * sub + 32 > kv_full_b[j]) {
+#pragma unroll
+                                for (int v = 0; v < 16; ++v)
+                                    s[j][sub][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
+                                                       ? s[j][sub][v] : -INFINITY;
+                            }
+                    }
+                    float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
+                    float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
+#pragma unroll
+                    for (int v = 3; v < 15; v += 2) {
+                        ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
+                        mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
+                    }
+                    float mx = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
+                    mx = half_swap_max(mx);
+                    m_raw[j] = fmaxf(m_raw[j], mx);
+                    saw[j] = saw[j] || (mx != -INFINITY);
+                    mx2[j] = mx * kScaleLog2;
+                    need_any = need_any || (mx2[j] > m_ref[j] + kTau);
+                }
+                if (__builtin_amdgcn_ballot_w64(need_any)) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
+                        const float alpha = (m_ref[j] == -INFINITY)
+                                                ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
+                        l_part[j] *= alpha;
+                        o[j][0] *= alpha;
+                        o[j][1] *= alpha;
+                        m_ref[j] = m_new;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
+                    float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter add chains
 #pragma unroll
                     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
                         for (int v = 0; v < 16; ++v) {
-                            const int kc = key0 + 32 * sub + 8 * (v >> 2) + 4 * g + (v & 3);
-                            const bool ok = q_ok[j] && kc < a.n_kv &&
-                                            (!a.causal || a.kv_pos0 + kc <= qpos[j]);
-                            s[j][sub][v] = ok ? s[j][sub][v] : -INFINITY;
+                            const float p = __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(s[j][sub][v], kScaleLog2, -base));
+                            s[j][sub][v] = p;
+                            ls[v & 3] += p;
                         }
+                    l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
                 }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    mx = fmaxf(mx, fmaxf(s[j][0][v], s[j][1][v]));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                m_raw[j] = fmaxf(m_raw[j], mx);
-                saw[j] = saw[j] || (mx != -INFINITY);
-                mx2[j] = mx * kScaleLog2;
-                need_any = need_any || (mx2[j] > m_ref[j] + kTau);
-            }
-            if (__builtin_amdgcn_ballot_w64(need_any)) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
-                    const float alpha =
-                        (m_ref[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
-                    l_part[j] *= alpha;
-                    o[j][0] *= alpha;
-                    o[j][1] *= alpha;
-                    m_ref[j] = m_new;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
-                float lsum = 0.f;
+                // O^T += V^T P^T; the V tile's key order matches the accumulator layout
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float p = __builtin_amdgcn_exp2f(
-                            __builtin_fmaf(s[j][sub][v], kScaleLog2, -base));
-                        s[j][sub][v] = p;
-                        lsum += p;
-                    }
-                l_part[j] += lsum;
-            }
-            // O^T += V^T P^T; the V tile's key order matches the accumulator layout
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const int pos = 32 * sub + 16 * tt + 8 * g;
-                    const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
-                    const half8 a1 =
-                        *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
-                    half8 sc0, sc1;
-                    if constexpr (FMT == 0) {
-                        sc0 = *reinterpret_cast<const half8 *>(&T.vsc[pos]);
-                        sc1 = *reinterpret_cast<const half8 *>(&T.vsc[KT + pos]);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const half8 p16 = to_half8(s[j][sub], 8 * tt);
-                        half8 b0 = p16, b1 = p16;
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int pos = 32 * sub + 16 * tt + 8 * g;
+                        const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
+                        const half8 a1 =
+                            *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
+                        half8 sc0, sc1;
                         if constexpr (FMT == 0) {
-                            b0 = p16 * sc0;
-                            b1 = p16 * sc1;
+                            sc0 = *reinterpret_cast<const half8 *>(&T.vsc[pos]);
+                            sc1 = *reinterpret_cast<const half8 *>(&T.vsc[KT + pos]);
                         }
-                        o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, o[j][0], 0, 0, 0);
-                        o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, o[j][1], 0, 0, 0);
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const half8 p16 = to_half8(s[j][sub], 8 * tt);
+                            half8 b0 = p16, b1 = p16;
+                            if constexpr (FMT == 0) {
+                                b0 = p16 * sc0;
+                                b1 = p16 * sc1;
+                            }
+                            o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, o[j][0], 0,
+                                                                             0, 0);
+                            o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, o[j][1], 0,
+                                                                             0, 0);
+                        }
                     }
-                }
+            }
         }
         if (t + 1 < n_tiles)
             unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
-                             sm.tile[(t + 1) & 1], tid);
+                             sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
         if (t + 2 < n_tiles)
             stash(t & 1);
         __syncthreads();
@@ -501,7 +536,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         if (kv_end_b[j] > 0) { // uniform per wavefront
-            const float l_tot = l_part[j] + __shfl_xor(l_part[j], 32);
+            const float l_tot = half_swap_sum(l_part[j]);
             if (q_ok[j] && saw[j]) {
                 const float rr = __builtin_amdgcn_exp2f(m_ref[j] - m_raw[j] * kScaleLog2);
                 float4 *orow = reinterpret_cast<float4 *>(a.o + row[j] * kHeadDim);

@@ -90,7 +90,9 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
  *   k, v     address of key 0 of the chunk for sequence 0, head 0.  Key j of (seq b, head h) is
  *            at  k + b*kv_seq_stride + h*kv_head_stride + j*row  (row = 68 bytes for Q8_0,
  *            128 for FP16).  16-byte aligned; both strides are byte counts, multiples of 16,
- *            and at least n_kv*row.
+ *            and at least n_kv*row.  Reads are 16-byte pieces: when n_kv*row is not a multiple
+ *            of 16, up to 12 bytes after a head's last key are read (never past the 16-byte
+ *            block holding that key's last byte) and ignored.
  *   kv_pos0  absolute position of chunk key 0 (>= 0);  n_kv  chunk length, >= 1 (a partial
  *            last chunk is fine).
  *   causal   1: the triangular mask of Mode A ("Out-of-Core ...", Sec. 4); 0: every chunk key
