@@ -15,8 +15,7 @@
 //       - K: the exact int8 values times the FP16 scale, split into two FP16 halves
 //         hi = fp16(q*d) and lo = q*d - hi (exact, q*d has at most 18 significant bits), so
 //         Q.K^T on FP16 MFMA reproduces the dequantised logits up to FP32 accumulation;
-//       - V: the exact int8 values as FP16, transposed to [dim][key]; its FP16 scales are kept
-//         per key and folded into the probabilities (P * d16, FP16) before the PV product.
+//       - V: fp16(q*d), transposed to [dim][key] (one rounding of the dequantised value).
 //   * Each wavefront owns two 32-row query blocks (w and 7 - w of the tile, which balances the
 //     causal diagonal) and computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so each lane
 //     holds 16 logits of ONE query per 32 keys: the row max needs one cross-lane step and the
@@ -120,8 +119,7 @@ template <int FMT> // 0: Q8_0 rows (68 bytes), 1: FP16 rows (128 bytes)
 struct KvTile {     // one LDS buffer of unpacked MFMA operands for KT keys
     _Float16 khi[KT * KP];                     // K (Q8_0: fp16(q*d)), [key][dim]
     _Float16 klo[FMT == 0 ? KT * KP : 8];      // Q8_0: q*d - khi, [key][dim]
-    _Float16 vt[64 * VP];                      // V int8 values (Q8_0) or V (FP16), [dim][vpos]
-    _Float16 vsc[FMT == 0 ? 2 * KT : 8];       // Q8_0 V scales, [block][vpos]
+    _Float16 vt[64 * VP];                      // V (Q8_0: fp16(q*d)), [dim][vpos]
 };
 
 template <int FMT>
@@ -186,6 +184,16 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                     x[c] = *reinterpret_cast<const uint32_t *>(rr + 36 + 4 * (dg - 8));
                 }
             }
+            // the four keys' scales of this block; keys past the chunk end get 0 (their raw
+            // bytes may be anything, and their P is 0)
+            _Float16 sc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const _Float16 d =
+                    *reinterpret_cast<const _Float16 *>(rv + (4 * kq + c) * 68 + 34 * blk);
+                sc[c] = 4 * kq + c < valid_keys ? d : (_Float16)0.0f;
+            }
+            const half2v s01 = {sc[0], sc[1]}, s23 = {sc[2], sc[3]};
             const int p0 = vpos(4 * kq);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -193,13 +201,10 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                                    (byte_of(x[2], d) << 16) | (byte_of(x[3], d) << 24);
                 half2v lo, hi;
                 i8x4_to_f16(y, lo, hi);
+                lo *= s01; // fp16(q * d): one rounding, like P * d in the product's B operand
+                hi *= s23;
                 const half4 r4 = {lo[0], lo[1], hi[0], hi[1]};
                 *reinterpret_cast<half4 *>(&T.vt[(4 * dg + d) * VP + p0]) = r4;
-            }
-            if (tid < 2 * KT) { // keys past the chunk end get scale 0 (their P is 0 too)
-                const int key = tid & 63, sb = tid >> 6;
-                const _Float16 d = *reinterpret_cast<const _Float16 *>(rv + key * 68 + 34 * sb);
-                T.vsc[sb * KT + vpos(key)] = key < valid_keys ? d : (_Float16)0.0f;
             }
         }
     } else {
@@ -479,12 +484,15 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                         m_ref[j] = m_new;
                     }
                 }
+                // l sums the FP32 probabilities (the FP16 rounding of P, the B operand of the PV
+                // product, would cost the log-sum-exp about 2^-12 relative on short rows)
+                half8 p16[2][2][2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
-                    float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter add chains
+                    float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
 #pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
+                    for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const float p = __builtin_amdgcn_exp2f(
@@ -492,6 +500,9 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                             s[j][sub][v] = p;
                             ls[v & 3] += p;
                         }
+                        p16[j][sub][0] = to_half8(s[j][sub], 0);
+                        p16[j][sub][1] = to_half8(s[j][sub], 8);
+                    }
                     l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
                 }
                 // O^T += V^T P^T; the V tile's key order matches the accumulator layout
@@ -503,23 +514,12 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                         const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
                         const half8 a1 =
                             *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
-                        half8 sc0, sc1;
-                        if constexpr (FMT == 0) {
-                            sc0 = *reinterpret_cast<const half8 *>(&T.vsc[pos]);
-                            sc1 = *reinterpret_cast<const half8 *>(&T.vsc[KT + pos]);
-                        }
 #pragma unroll
                         for (int j = 0; j < 2; ++j) {
-                            const half8 p16 = to_half8(s[j][sub], 8 * tt);
-                            half8 b0 = p16, b1 = p16;
-                            if constexpr (FMT == 0) {
-                                b0 = p16 * sc0;
-                                b1 = p16 * sc1;
-                            }
-                            o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, o[j][0], 0,
-                                                                             0, 0);
-                            o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, o[j][1], 0,
-                                                                             0, 0);
+                            o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                a0, p16[j][sub][tt], o[j][0], 0, 0, 0);
+                            o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                a1, p16[j][sub][tt], o[j][1], 0, 0, 0);
                         }
                     }
             }
