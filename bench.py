@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "causal prefill attention TFLOP/s & % of MI355X FP16 MFMA peak (Q8_0 KV)"
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense FP16 MFMA
 PEAK_HBM_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "accumulate_batch8_m2048_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "accumulate_batch8_m2048_traffic.txt")
 KERNEL_SOURCES = ["chunked_flashattention_q8_amd/csrc/attn.hip",
                   "chunked_flashattention_q8_amd/csrc/q8attn_internal.h"]
 
@@ -209,16 +209,97 @@ def cpu_baseline(w, res, kv_dtype, budget_s):
     return base, parity
 
 
+def read_summary(path):
+    """'key: value' lines of a profiles/ summary ('#' lines are comments)."""
+    out = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("#") or ":" not in ln:
+                continue
+            k, v = ln.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
 def traffic_per_launch():
+    """HBM bytes per accumulate launch from the committed counter summary, or None when there
+    is none or the kernel source changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    try:
-        t = json.load(open(TRAFFIC_FILE))
-    except ValueError:
-        return None
+    t = read_summary(TRAFFIC_FILE)
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return float(t["hbm_bytes_per_launch"])
+
+
+def algorithmic_bytes(w, chunk):
+    """Algorithmic HBM bytes of each chunk call: the chunk's K and V rows (136 B per key per
+    head), Q rows of the queries that see the chunk (128 B), their state read (m; l and O only
+    for rows that are not empty) and written (m, l, O: 264 B)."""
+    import numpy as np
+    pos = w.q_pos0 + np.arange(w.M, dtype=np.int64)
+    out = []
+    for s in range(0, w.N, chunk):
+        n = min(chunk, w.N - s)
+        touched = int((pos >= s).sum())
+        nonempty = int((pos >= s).sum()) if s > 0 else 0  # every row sees key 0 first
+        per_head = n * 136 + touched * (128 + 4 + 264) + nonempty * 260
+        out.append(per_head * w.B * w.H)
+    return out
+
+
+def counter_means(d, counter, name_part):
+    """Mean over the dispatches whose kernel name contains name_part of the summed counter."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s samples for kernels named *%s* under %s" % (counter, name_part, d))
+    return sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mib, commands):
+    """Write the HBM traffic summary of the accumulate kernel from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the default workload, and of a plain copy
+    of cal_mib MiB, which scales each counter to bytes."""
+    import synthetic
+    w = synthetic.WORKLOADS[2]
+    fetch, n_f = counter_means(fetch_dir, "FETCH_SIZE", "accumulate_kernel<0>")
+    write, n_w = counter_means(write_dir, "WRITE_SIZE", "accumulate_kernel<0>")
+    cf, _ = counter_means(cal_fetch_dir, "FETCH_SIZE", "copy")
+    cw, _ = counter_means(cal_write_dir, "WRITE_SIZE", "copy")
+    copy_bytes = cal_mib * (1 << 20)
+    f_fac, w_fac = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    hbm = fetch * 1024 * f_fac + write * 1024 * w_fac
+    alg = algorithmic_bytes(w, w.chunk)
+    lines = [
+        "# HBM traffic of accumulate_kernel<0> (Q8_0 KV) per launch, batch8_m2048 workload:",
+        "# 8 sequences x 32 heads, M = N = 2048 causal, d = 64, B_C = 512 (4 launches per step).",
+        "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, averaged over the accumulate dispatches;",
+        "# each is scaled by (bytes copied) / (counter x 1024) of a plain device copy of",
+        "# %d MiB (torch copy kernel), measured the same way." % cal_mib,
+        "# commands (repository root on an MI355X):",
+    ] + ["#   " + c for c in commands] + [
+        "#   python bench.py --traffic-summary <the four -d folders above> %d" % cal_mib,
+        "kernel_source_sha256: %s" % kernel_source_hash(),
+        "dispatches_fetch: %d" % n_f,
+        "dispatches_write: %d" % n_w,
+        "fetch_kib_per_launch: %.1f" % fetch,
+        "write_kib_per_launch: %.1f" % write,
+        "copy_fetch_factor: %.4f" % f_fac,
+        "copy_write_factor: %.4f" % w_fac,
+        "hbm_bytes_per_launch: %.0f" % hbm,
+        "algorithmic_bytes_per_launch: %.0f" % (sum(alg) / len(alg)),
+        "algorithmic_bytes_per_chunk_call: %s" % " ".join(str(a) for a in alg),
+        "traffic_over_algorithmic: %.3f" % (hbm / (sum(alg) / len(alg))),
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -232,7 +313,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--traffic-summary", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "MIB"),
+                    help="write the accumulate kernel's HBM traffic summary from rocprofv3 runs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        fd, wd, cfd, cwd, mib = args.traffic_summary
+        cmds = ["rocprofv3 --pmc FETCH_SIZE -d %s -o f --output-format csv -- "
+                "python bench.py --no-cpu-baseline --steps 3 --warmup 1" % fd,
+                "rocprofv3 --pmc WRITE_SIZE -d %s -o w --output-format csv -- "
+                "python bench.py --no-cpu-baseline --steps 3 --warmup 1" % wd,
+                "rocprofv3 --pmc FETCH_SIZE -d %s -o cf --output-format csv -- "
+                "python bench.py --copy-calibration %s" % (cfd, mib),
+                "rocprofv3 --pmc WRITE_SIZE -d %s -o cw --output-format csv -- "
+                "python bench.py --copy-calibration %s" % (cwd, mib)]
+        traffic_summary(fd, wd, cfd, cwd, int(mib), cmds)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

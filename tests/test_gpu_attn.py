@@ -1,6 +1,6 @@
 """GPU chunked causal attention against the FP64 oracle, element by element, through the C ABI.
 
-Small cases span several 128-query workgroups and 64-key tiles and end in ragged tails (query
+Small cases span several query workgroups and 64-key tiles and end in ragged tails (query
 counts that leave partial wavefronts, chunk lengths whose byte size is not a multiple of 16);
 the edge cases are a single key, chunks no query can see, non-causal chunks, shuffled chunk
 order, checkpoint/resume and the empty state."""
