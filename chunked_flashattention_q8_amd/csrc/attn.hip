@@ -136,21 +136,20 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                                             int tid, int valid_keys)
 {
     if constexpr (FMT == 0) {
-        { // K: thread = (block, key, 16-value half); waves 0-1 block 0, waves 2-3 block 1
+        { // K: thread = (block, key, 16-value half); waves 0-1 block 0, waves 2-3 block 1.
+            // The 16 values sit at byte 34*blk + 2 + 16*hh of the row: read the 5 dwords that
+            // cover them and realign (by 2 bytes for block 0, none for block 1).  No branches,
+            // so this work can be scheduled among the matrix instructions.
             const int blk = tid >> 7, key = (tid & 127) >> 1, hh = tid & 1;
             const uint8_t *rr = rk + key * 68;
+            const int off = 34 * blk + 2 + 16 * hh, sh = off & 3;
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + (off & ~3));
+            const uint32_t x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3], x4 = p[4];
             uint32_t w[4];
-            if (blk == 0) { // values at byte 2 + 16*hh: realign by 2 bytes
-                const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 16 * hh);
-                const uint32_t x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3], x4 = p[4];
-                w[0] = __builtin_amdgcn_alignbyte(x1, x0, 2);
-                w[1] = __builtin_amdgcn_alignbyte(x2, x1, 2);
-                w[2] = __builtin_amdgcn_alignbyte(x3, x2, 2);
-                w[3] = __builtin_amdgcn_alignbyte(x4, x3, 2);
-            } else {        // values at byte 36 + 16*hh: dword aligned
-                const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 36 + 16 * hh);
-                w[0] = p[0]; w[1] = p[1]; w[2] = p[2]; w[3] = p[3];
-            }
+            w[0] = __builtin_amdgcn_alignbyte(x1, x0, sh);
+            w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh);
+            w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh);
+            w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh);
             const _Float16 d = *reinterpret_cast<const _Float16 *>(rr + 34 * blk);
             const half2v d2 = {d, d};
             half8 hi8[2], lo8[2];
@@ -172,17 +171,16 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             dl[0] = lo8[0]; dl[1] = lo8[1];
         }
         { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
+            // dims 4*dg .. 4*dg+3 sit at byte 2 + 4*dg + 2*blk of the row (block 1 skips the
+            // second scale): realign by 2 bytes for block 0, none for block 1
             const int kq = tid & 15, dg = tid >> 4, blk = dg >> 3;
+            const int off = 2 + 4 * dg + 2 * blk, sh = off & 3;
             uint32_t x[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint8_t *rr = rv + (4 * kq + c) * 68;
-                if (blk == 0) {
-                    const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + 4 * dg);
-                    x[c] = __builtin_amdgcn_alignbyte(p[1], p[0], 2);
-                } else {
-                    x[c] = *reinterpret_cast<const uint32_t *>(rr + 36 + 4 * (dg - 8));
-                }
+                const uint32_t *p =
+                    reinterpret_cast<const uint32_t *>(rv + (4 * kq + c) * 68 + (off & ~3));
+                x[c] = __builtin_amdgcn_alignbyte(p[1], p[0], sh);
             }
             // the four keys' scales of this block; keys past the chunk end get 0 (their raw
             // bytes may be anything, and their P is 0)
@@ -295,6 +293,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         row[j] = head * a.M + qi[j];
     }
     const int kv_end_w = max(kv_end_b[0], kv_end_b[1]);
+    const int kv_full_w = min(kv_full_b[0], kv_full_b[1]); // keys every row of the wave sees
 
     half8 qreg[2][4];
     floatx16 o[2][2];
@@ -392,120 +391,126 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         }
     };
 
+    // Loads past the chunk read as zero, and operand tiles unpacked from raw rows past the last
+    // tile are never read, so fetch / stash / unpack run unconditionally (no branches inside
+    // the tile loop's scheduling regions).
     fetch(0);
     stash(0);
-    if (n_tiles > 1) {
-        fetch(1);
-        stash(1);
-    }
+    fetch(1);
+    stash(1);
     __syncthreads();
     unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
     __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
-        if (t + 2 < n_tiles)
-            fetch(t + 2);
+        fetch(t + 2);
         const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
+        // tile t+1 is unpacked from its raw rows in every branch: the same barrier interval
+        // that reads operand buffer t&1 writes buffer (t+1)&1
         if (key0 < kv_end_w) {
-            // One 64-key tile for both query blocks.  The 32-key subtiles that some row of a
-            // block cannot wholly see (causal diagonal, ragged chunk end, padding rows) are masked
-            // element by element; the others -- the common case -- are not touched.
-            {
-                // S^T = K Q^T: lane (qcol, g) holds
-                // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][sub][v]
-                floatx16 s[2][2];
+            // S^T = K Q^T: lane (qcol, g) holds
+            // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][sub][v]
+            floatx16 s[2][2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
+                for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            s[j][sub][v] = 0.f;
+                    for (int v = 0; v < 16; ++v)
+                        s[j][sub][v] = 0.f;
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    const int kr = (32 * sub + qcol) * KP + 8 * g;
+            for (int sub = 0; sub < 2; ++sub) {
+                const int kr = (32 * sub + qcol) * KP + 8 * g;
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[j][kk],
+                                                                          s[j][sub], 0, 0, 0);
+                    if constexpr (FMT == 0) {
+                        const half8 al = *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
 #pragma unroll
                         for (int j = 0; j < 2; ++j)
                             s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                ah, qreg[j][kk], s[j][sub], 0, 0, 0);
-                        if constexpr (FMT == 0) {
-                            const half8 al =
-                                *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
-#pragma unroll
-                            for (int j = 0; j < 2; ++j)
-                                s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                    al, qreg[j][kk], s[j][sub], 0, 0, 0);
-                        }
+                                al, qreg[j][kk], s[j][sub], 0, 0, 0);
                     }
                 }
-                bool need_any = false;
-                float mx2[2];
+            }
+            // independent VALU work for the matrix instructions above to overlap with
+            unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
+                             sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
+
+            // The 32-key subtiles that some row of a block cannot wholly see (causal diagonal,
+            // ragged chunk end, padding rows) are masked element by element; the common case
+            // skips this with one wavefront-uniform test.
+            if (key0 + KT > kv_full_w) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    {
-                        // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
-                        const int rel = lim[j] - key0 - 4 * g;
+                    // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
+                    const int rel = lim[j] - key0 - 4 * g;
 #pragma unroll
-                        for (int sub = 0; sub < 2; ++sub)
-                            if (key0 + 32 * sub + 32 > kv_full_b[j]) {
+                    for (int sub = 0; sub < 2; ++sub)
+                        if (key0 + 32 * sub + 32 > kv_full_b[j]) {
 #pragma unroll
-                                for (int v = 0; v < 16; ++v)
-                                    s[j][sub][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
-                                                       ? s[j][sub][v] : -INFINITY;
-                            }
-                    }
-                    float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
-                    float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
-#pragma unroll
-                    for (int v = 3; v < 15; v += 2) {
-                        ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
-                        mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
-                    }
-                    float mx = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
-                    mx = half_swap_max(mx);
-                    m_raw[j] = fmaxf(m_raw[j], mx);
-                    saw[j] = saw[j] || (mx != -INFINITY);
-                    mx2[j] = mx * kScaleLog2;
-                    need_any = need_any || (mx2[j] > m_ref[j] + kTau);
+                            for (int v = 0; v < 16; ++v)
+                                s[j][sub][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
+                                                   ? s[j][sub][v] : -INFINITY;
+                        }
                 }
-                if (__builtin_amdgcn_ballot_w64(need_any)) {
+            }
+            bool need_any = false;
+            float mx2[2];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
-                        const float alpha = (m_ref[j] == -INFINITY)
-                                                ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
-                        l_part[j] *= alpha;
-                        o[j][0] *= alpha;
-                        o[j][1] *= alpha;
-                        m_ref[j] = m_new;
-                    }
+            for (int j = 0; j < 2; ++j) {
+                float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
+                float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
+#pragma unroll
+                for (int v = 3; v < 15; v += 2) {
+                    ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
+                    mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
                 }
-                // l sums the FP32 probabilities (the FP16 rounding of P, the B operand of the PV
-                // product, would cost the log-sum-exp about 2^-12 relative on short rows)
-                half8 p16[2][2][2];
+                float mx = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
+                mx = half_swap_max(mx);
+                m_raw[j] = fmaxf(m_raw[j], mx);
+                saw[j] = saw[j] || (mx != -INFINITY);
+                mx2[j] = mx * kScaleLog2;
+                need_any = need_any || (mx2[j] > m_ref[j] + kTau);
+            }
+            if (__builtin_amdgcn_ballot_w64(need_any)) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
-                    float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
-#pragma unroll
-                    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const float p = __builtin_amdgcn_exp2f(
-                                __builtin_fmaf(s[j][sub][v], kScaleLog2, -base));
-                            s[j][sub][v] = p;
-                            ls[v & 3] += p;
-                        }
-                        p16[j][sub][0] = to_half8(s[j][sub], 0);
-                        p16[j][sub][1] = to_half8(s[j][sub], 8);
-                    }
-                    l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+                    const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
+                    const float alpha = (m_ref[j] == -INFINITY)
+                                            ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
+                    l_part[j] *= alpha;
+                    o[j][0] *= alpha;
+                    o[j][1] *= alpha;
+                    m_ref[j] = m_new;
                 }
-                // O^T += V^T P^T; the V tile's key order matches the accumulator layout
+            }
+            // per query block: P = exp2(S*log2e/8 - ref) (l sums the FP32 values), P to FP16,
+            // then O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
+                float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
+                half8 p16[2][2];
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const float p = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(s[j][sub][v], kScaleLog2, -base));
+                        s[j][sub][v] = p;
+                        ls[v & 3] += p;
+                    }
+                    p16[sub][0] = to_half8(s[j][sub], 0);
+                    p16[sub][1] = to_half8(s[j][sub], 8);
+                }
+                l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+                // the V tile's key order matches the accumulator layout
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -514,21 +519,17 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                         const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
                         const half8 a1 =
                             *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                a0, p16[j][sub][tt], o[j][0], 0, 0, 0);
-                            o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                a1, p16[j][sub][tt], o[j][1], 0, 0, 0);
-                        }
+                        o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p16[sub][tt],
+                                                                         o[j][0], 0, 0, 0);
+                        o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p16[sub][tt],
+                                                                         o[j][1], 0, 0, 0);
                     }
             }
-        }
-        if (t + 1 < n_tiles)
+        } else {
             unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
-        if (t + 2 < n_tiles)
-            stash(t & 1);
+        }
+        stash(t & 1); // raw rows of tile t+2 (raw buffer t&1 was unpacked in the last interval)
         __syncthreads();
     }
 
