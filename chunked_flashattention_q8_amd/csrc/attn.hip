@@ -63,19 +63,24 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Four signed bytes -> four FP16 values (exact).  Each byte is biased to unsigned, placed in the
-// mantissa of 1024.0 (0x6400), and 1024 + 128 is subtracted.
+// Signed bytes -> FP16 values (exact).  Each byte is biased to unsigned (x ^ 0x80) and placed as
+// the low mantissa byte of 1024.0 (0x64 high byte), giving 1024 + 128 + x; subtracting 1152
+// leaves x.  v_perm_b32 picks bytes from {S0, S1} (selector 0-3: S1's bytes, 4-7: S0's), so
+// with S0 = 0x64646464 one instruction builds two such FP16 values.
+constexpr uint32_t kF16Magic = 0x64646464u;
+__device__ __forceinline__ half2v biased_pair_to_f16(uint32_t u, uint32_t sel)
+{
+    const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kF16Magic, u, sel)) - bias;
+}
+
+// four signed bytes of w -> (bytes 0, 1) and (bytes 2, 3) as FP16 pairs
 __device__ __forceinline__ void i8x4_to_f16(uint32_t w, half2v &lo, half2v &hi)
 {
     const uint32_t u = w ^ 0x80808080u;
-    const uint32_t a = (u & 0xffu) | ((u & 0xff00u) << 8) | 0x64006400u;
-    const uint32_t b = ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u) | 0x64006400u;
-    const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    lo = __builtin_bit_cast(half2v, a) - bias;
-    hi = __builtin_bit_cast(half2v, b) - bias;
+    lo = biased_pair_to_f16(u, 0x04010400u);
+    hi = biased_pair_to_f16(u, 0x04030402u);
 }
-
-__device__ __forceinline__ uint32_t byte_of(uint32_t x, int i) { return (x >> (8 * i)) & 0xffu; }
 
 // Position of key r (0..63) inside the transposed V tile and the V-scale vector: bits 2 and 3
 // swapped, so that the 8 keys one lane contributes to a PV step are contiguous.
@@ -192,15 +197,22 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                 sc[c] = 4 * kq + c < valid_keys ? d : (_Float16)0.0f;
             }
             const half2v s01 = {sc[0], sc[1]}, s23 = {sc[2], sc[3]};
+            // byte transpose: t01[i] interleaves the bytes of keys 0 and 1 for dims 2i, 2i+1
+            // ([k0.d, k1.d, k0.d+1, k1.d+1]), t23[i] those of keys 2 and 3; each FP16 pair
+            // (key 0, key 1) or (key 2, key 3) of one dim is then one byte pick.
+            const uint32_t u0 = x[0] ^ 0x80808080u, u1 = x[1] ^ 0x80808080u;
+            const uint32_t u2 = x[2] ^ 0x80808080u, u3 = x[3] ^ 0x80808080u;
+            const uint32_t t01[2] = {__builtin_amdgcn_perm(u1, u0, 0x05010400u),
+                                     __builtin_amdgcn_perm(u1, u0, 0x07030602u)};
+            const uint32_t t23[2] = {__builtin_amdgcn_perm(u3, u2, 0x05010400u),
+                                     __builtin_amdgcn_perm(u3, u2, 0x07030602u)};
             const int p0 = vpos(4 * kq);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint32_t y = byte_of(x[0], d) | (byte_of(x[1], d) << 8) |
-                                   (byte_of(x[2], d) << 16) | (byte_of(x[3], d) << 24);
-                half2v lo, hi;
-                i8x4_to_f16(y, lo, hi);
-                lo *= s01; // fp16(q * d): one rounding, like P * d in the product's B operand
-                hi *= s23;
+                const uint32_t sel = (d & 1) ? 0x04030402u : 0x04010400u;
+                // fp16(q * d): one rounding, like P * d in the product's B operand
+                const half2v lo = biased_pair_to_f16(t01[d >> 1], sel) * s01;
+                const half2v hi = biased_pair_to_f16(t23[d >> 1], sel) * s23;
                 const half4 r4 = {lo[0], lo[1], hi[0], hi[1]};
                 *reinterpret_cast<half4 *>(&T.vt[(4 * dg + d) * VP + p0]) = r4;
             }
@@ -372,38 +384,41 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             return true;
         }
     };
-    auto fetch = [&](int t) {
+    auto fetch = [&](int t, u32x4 (&dst)[NPRE]) {
 #pragma unroll
         for (int sl = 0; sl < NPRE; ++sl) {
             int tensor, piece;
             if (slot(sl, tensor, piece)) {
                 const uint32_t off = (uint32_t)t * (KT * ROW) + 16u * piece;
-                pre[sl] = load16(tensor ? rv : rk, off);
+                dst[sl] = load16(tensor ? rv : rk, off);
             }
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, const u32x4 (&src)[NPRE]) {
 #pragma unroll
         for (int sl = 0; sl < NPRE; ++sl) {
             int tensor, piece;
             if (slot(sl, tensor, piece))
-                *reinterpret_cast<u32x4 *>(&sm.raw[buf][tensor][16 * piece]) = pre[sl];
+                *reinterpret_cast<u32x4 *>(&sm.raw[buf][tensor][16 * piece]) = src[sl];
         }
     };
 
     // Loads past the chunk read as zero, and operand tiles unpacked from raw rows past the last
     // tile are never read, so fetch / stash / unpack run unconditionally (no branches inside
     // the tile loop's scheduling regions).
-    fetch(0);
-    stash(0);
-    fetch(1);
-    stash(1);
+    {
+        u32x4 pre1[NPRE]; // both prologue tiles are in flight at once
+        fetch(0, pre);
+        fetch(1, pre1);
+        stash(0, pre);
+        stash(1, pre1);
+    }
     __syncthreads();
     unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
     __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
-        fetch(t + 2);
+        fetch(t + 2, pre);
         const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
         // tile t+1 is unpacked from its raw rows in every branch: the same barrier interval
@@ -529,7 +544,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
         }
-        stash(t & 1); // raw rows of tile t+2 (raw buffer t&1 was unpacked in the last interval)
+        stash(t & 1, pre); // raw rows of tile t+2 (raw buffer t&1 was unpacked in the last interval)
         __syncthreads();
     }
 
