@@ -3,7 +3,7 @@
 //
 // HBM-bound: each 32-value block reads 128 bytes and writes 34.  Eight consecutive lanes own one
 // block and each loads one 16-byte float4, so a wavefront reads 1 KiB of contiguous input per
-// instruction.  The block's largest magnitude is reduced over the eight lanes, every lane derives
+// instruction; every lane handles two blocks, 256 float4 apart, with both loads in flight.  The block's largest magnitude is reduced over the eight lanes, every lane derives
 // the same FP16 scale, quantises its four values and writes them as two 16-bit stores (block
 // starts are 2-byte aligned: 34 * k).
 //
@@ -27,34 +27,42 @@ __device__ __forceinline__ int quantise(float x, float dh)
     return (int)r;
 }
 
+// Each lane packs its quarter of U blocks (U x 256 consecutive float4 per workgroup); the U loads
+// are issued before any is used.
+template <int U>
 __global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict__ x,
                                                          uint8_t *__restrict__ dst,
                                                          int64_t n_blocks)
 {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = gid >> 3;
-    const int sub = (int)(gid & 7);
-    const bool valid = blk < n_blocks;
-    float4 v = valid ? x[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
-
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, __shfl_xor(a, 1, 8));
-    a = fmaxf(a, __shfl_xor(a, 2, 8));
-    a = fmaxf(a, __shfl_xor(a, 4, 8));
-
-    const __half d16 = __float2half_rn(__fdiv_rn(a, 127.0f));
-    const float dh = __half2float(d16);
-    const int q0 = quantise(v.x, dh), q1 = quantise(v.y, dh);
-    const int q2 = quantise(v.z, dh), q3 = quantise(v.w, dh);
-    if (!valid)
-        return;
-
-    uint8_t *out = dst + blk * 34;
-    if (sub == 0)
-        *reinterpret_cast<uint16_t *>(out) = __half_as_ushort(d16);
-    uint16_t *o16 = reinterpret_cast<uint16_t *>(out + 2 + 4 * sub);
-    o16[0] = (uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8));
-    o16[1] = (uint16_t)((q2 & 0xff) | ((q3 & 0xff) << 8));
+    float4 v[U];
+    int64_t blk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t gid = ((int64_t)blockIdx.x * U + u) * 256 + threadIdx.x;
+        blk[u] = gid >> 3;
+        v[u] = blk[u] < n_blocks ? x[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int sub = (int)(threadIdx.x & 7);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float a = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)),
+                        fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+        a = fmaxf(a, __shfl_xor(a, 1, 8));
+        a = fmaxf(a, __shfl_xor(a, 2, 8));
+        a = fmaxf(a, __shfl_xor(a, 4, 8));
+        const __half d16 = __float2half_rn(__fdiv_rn(a, 127.0f));
+        const float dh = __half2float(d16);
+        const int q0 = quantise(v[u].x, dh), q1 = quantise(v[u].y, dh);
+        const int q2 = quantise(v[u].z, dh), q3 = quantise(v[u].w, dh);
+        if (blk[u] < n_blocks) {
+            uint8_t *out = dst + blk[u] * 34;
+            if (sub == 0)
+                *reinterpret_cast<uint16_t *>(out) = __half_as_ushort(d16);
+            uint16_t *o16 = reinterpret_cast<uint16_t *>(out + 2 + 4 * sub);
+            o16[0] = (uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8));
+            o16[1] = (uint16_t)((q2 & 0xff) | ((q3 & 0xff) << 8));
+        }
+    }
 }
 
 } // namespace
@@ -63,9 +71,10 @@ hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipS
 {
     if (n_blocks == 0)
         return hipSuccess;
+    constexpr int U = 2; // blocks per lane group of 8 (two 16-byte loads in flight per lane)
     const int64_t threads = n_blocks * 8;
-    const int64_t grid = (threads + 255) / 256;
-    hipLaunchKernelGGL(q8_0_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+    const int64_t grid = (threads + 256 * U - 1) / (256 * U);
+    hipLaunchKernelGGL(q8_0_pack_kernel<U>, dim3((unsigned)grid), dim3(256), 0, s,
                        reinterpret_cast<const float4 *>(x), dst, n_blocks);
     return hipGetLastError();
 }
