@@ -80,6 +80,7 @@ def _load():
     lib.orc_attention_chunks.argtypes = [ctypes.POINTER(_Problem), P, i64, P, P, ctypes.c_int,
                                          P, P, P, ctypes.c_int]
     lib.orc_finalize.argtypes = [P, P, P, i64, ctypes.c_int, P, P]
+    lib.orc_merge_states.argtypes = [P, P, P, P, P, P, i64, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -237,6 +238,22 @@ def attention_chunks(prob: Problem, chunks, rows=None, state=None,
                                           nthreads or default_threads())
         if rc:
             raise MemoryError("oracle allocation failed")
+    return m, l, O
+
+
+def merge_states(a, b):
+    """Merge partial state b (m, l, O) into a copy of partial state a, both over the same rows
+    and disjoint key sets: the state a single pass over both key sets reaches."""
+    m = np.array(a[0], dtype=np.float64, copy=True)
+    l = np.array(a[1], dtype=np.float64, copy=True)
+    O = np.ascontiguousarray(np.array(a[2], dtype=np.float64, copy=True))
+    mb = np.ascontiguousarray(np.asarray(b[0], dtype=np.float64))
+    lb = np.ascontiguousarray(np.asarray(b[1], dtype=np.float64))
+    Ob = np.ascontiguousarray(np.asarray(b[2], dtype=np.float64))
+    if mb.shape != m.shape or Ob.shape != O.shape:
+        raise ValueError("states of different shapes")
+    n, D = O.shape
+    _load().orc_merge_states(_ptr(m), _ptr(l), _ptr(O), _ptr(mb), _ptr(lb), _ptr(Ob), n, D)
     return m, l, O
 
 

@@ -485,6 +485,34 @@ int orc_attention_chunks(const orc_problem *p, const int64_t *rows, int64_t n_ro
     return run_rows(p, rows, n_rows, 1, O, NULL, c_start, c_len, n_chunks, m, l, nthreads);
 }
 
+/* Merge two partial states of the same rows, over disjoint key sets, into the first: the state
+ * a single pass over both key sets would have reached.  A partial state (m, l, O) summarises its
+ * keys exactly as a chunk's (local maximum, sum of e^(S - max), sum of e^(S - max) V) do, so this
+ * is steps 3-6 of the [OOC] Sec. 3 recurrence with the second state in the chunk's place:
+ * m' = max(m_a, m_b), l' = l_a e^(m_a - m') + l_b e^(m_b - m'), O' likewise.  An empty state
+ * (m = -inf) contributes nothing; two empty states stay empty. */
+void orc_merge_states(double *m_a, double *l_a, double *O_a, const double *m_b,
+                      const double *l_b, const double *O_b, int64_t n_rows, int D)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        if (m_b[r] == -INFINITY)
+            continue;
+        if (m_a[r] == -INFINITY) {
+            m_a[r] = m_b[r];
+            l_a[r] = l_b[r];
+            for (int t = 0; t < D; ++t)
+                O_a[r * D + t] = O_b[r * D + t];
+            continue;
+        }
+        double mn = m_a[r] > m_b[r] ? m_a[r] : m_b[r];
+        double fa = exp(m_a[r] - mn), fb = exp(m_b[r] - mn);
+        l_a[r] = l_a[r] * fa + l_b[r] * fb;
+        for (int t = 0; t < D; ++t)
+            O_a[r * D + t] = O_a[r * D + t] * fa + O_b[r * D + t] * fb;
+        m_a[r] = mn;
+    }
+}
+
 /* After the last chunk the output is O / l ([OOC] Sec. 3) and the log-sum-exp is m + ln l.
  * A row that never saw a key (l = 0) yields O = 0 and LSE = -inf. */
 void orc_finalize(const double *m, const double *l, const double *O, int64_t n_rows, int D,

@@ -186,3 +186,35 @@ def test_chunk_without_visible_keys_leaves_state_untouched(orc):
     assert np.all(np.isneginf(st3[0])) and not st3[1].any() and not st3[2].any()
     out, lse = orc.finalize(*st3)
     assert not out.any() and np.all(np.isneginf(lse))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_merged_partial_states_equal_attention_over_the_union(orc, causal):
+    """Partial states over disjoint key ranges, merged, give the single-pass attention over all
+    keys (torch's float64 SDPA), for a split into 2 and into 5 ranges merged in shuffled order;
+    rows that see none of a range's keys keep the other state."""
+    M, N, q_pos0 = 30, 160, 120
+    prob, qd, kd, vd = make(orc, 1, 3, M, N, q_pos0, seed=77, causal=causal)
+    o_ref, lse_ref, _ = torch_ref(qd, kd, vd, q_pos0, causal)
+    for cuts in ([0, 70, N], [0, 13, 40, 99, 141, N]):
+        parts = [orc.attention_chunks(prob, [(a, b - a)]) for a, b in zip(cuts[:-1], cuts[1:])]
+        order = np.random.default_rng(len(cuts)).permutation(len(parts))
+        st = parts[order[0]]
+        for i in order[1:]:
+            st = orc.merge_states(st, parts[i])
+        O, lse = orc.finalize(*st)
+        np.testing.assert_allclose(O, o_ref.reshape(-1, D), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref.reshape(-1), rtol=1e-13, atol=1e-12)
+
+
+def test_merge_with_an_empty_state_is_the_identity(orc):
+    M, N, q_pos0 = 12, 64, 20
+    prob, *_ = make(orc, 1, 2, M, N, q_pos0, seed=5)
+    st = orc.attention_chunks(prob, [(0, 40)])
+    empty = orc.init_state(st[0].size, D)
+    for a, b in ((st, empty), (empty, st)):
+        out = orc.merge_states(a, b)
+        for x, y in zip(out, st):
+            assert np.array_equal(x, y)
+    both = orc.merge_states(empty, empty)
+    assert np.all(np.isneginf(both[0])) and not both[1].any() and not both[2].any()
