@@ -160,6 +160,134 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
     return res
 
 
+def build_streamed_cache(w):
+    """Q8_0 K and V of a streamed workload, drawn and packed chunk by chunk (the FP32 cache never
+    exists whole): a device-resident copy [C, 1, H, chunk, 68] and the pinned host copy."""
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    H, C, chunk = w.H, w.n_chunks, w.chunk
+    row = q8a.ROW_BYTES[q8a.KV_Q8_0]
+    kh = torch.empty((C, 1, H, chunk, row), dtype=torch.uint8, pin_memory=True)
+    vh = torch.empty(kh.shape, dtype=torch.uint8, pin_memory=True)
+    kd = torch.empty(kh.shape, dtype=torch.uint8, device=dev)
+    vd = torch.empty_like(kd)
+    for c in range(C):
+        k, v = synthetic.gen_kv_chunk(w, c)
+        n = k.shape[1]
+        q8a.q8_0_pack(torch.from_numpy(k).to(dev), kd[c, 0, :, :n], H * n, w.D)
+        q8a.q8_0_pack(torch.from_numpy(v).to(dev), vd[c, 0, :, :n], H * n, w.D)
+        kh[c].copy_(kd[c])
+        vh[c].copy_(vd[c])
+        if c % 16 == 15:
+            print("packed chunk %d of %d" % (c + 1, C), file=sys.stderr, flush=True)
+    return kd, vd, kh, vh
+
+
+def run_burst(w, steps, warmup, n_split):
+    """Mode B burst verification: 64 queries over the whole 1M-token cache, no causal mask.
+    Resident: the key range is split into n_split consecutive ranges that one state holds as
+    n_split "sequences" (the same queries repeated, the sequence stride stepping from one key
+    range to the next), so every chunk call works on all ranges at once; the sequence blocks are
+    then merged pairwise (attn_state_merge on sub-state descriptors, log2(n_split) launches) and
+    sequence 0 is finalized.  Streamed: one state fed through two device slots from pinned host
+    memory, as for the prefill workload."""
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    H, C, chunk, M = w.H, w.n_chunks, w.chunk, w.M
+    if C % n_split or n_split & (n_split - 1):
+        raise ValueError("n_split must be a power of two dividing the chunk count")
+    per = C // n_split  # chunks per key range
+    row = q8a.ROW_BYTES[q8a.KV_Q8_0]
+    kd, vd, kh, vh = build_streamed_cache(w)
+    qd = torch.from_numpy(synthetic.gen_q(w)).view(torch.float16).to(dev)
+    qrep = qd.expand(n_split, H, M, w.D).contiguous()
+    chunk_bytes = H * chunk * row
+    m, l, o = q8a.alloc_state(n_split, H, M, dev)
+    out = torch.empty((1, H, M, w.D), dtype=torch.float16, device=dev)
+    lse = torch.empty((1, H, M), dtype=torch.float32, device=dev)
+    slots_k = [torch.empty(chunk_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    slots_v = [torch.empty(chunk_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    main = torch.cuda.Stream()
+    copy_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def split():
+        st = q8a.attn_state_init(m, l, o, n_split, H, M, w.D, w.q_pos0, main)
+        for c in range(per):  # chunk c of every key range r (global chunk r * per + c)
+            q8a.attn_accumulate_chunk(st, qrep, kd[c].data_ptr(), vd[c].data_ptr(),
+                                      q8a.KV_Q8_0, c * chunk, chunk, chunk * row,
+                                      per * chunk_bytes, 0, main)
+        n = n_split
+        while n > 1:
+            n //= 2
+            q8a.attn_state_merge(q8a.sub_state(st, 0, n), q8a.sub_state(st, n, n), main)
+        q8a.attn_finalize(q8a.sub_state(st, 0, 1), out, lse, main)
+
+    def streamed():
+        st = q8a.attn_state_init(m[:1], l[:1], o[:1], 1, H, M, w.D, w.q_pos0, main)
+        q8a.attn_accumulate_stream(st, qd, kh, vh, q8a.KV_Q8_0, w.N, chunk, slots_k, slots_v, 0,
+                                   main, copy_stream)
+        q8a.attn_finalize(st, out, lse, main)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        for _ in range(steps):
+            fn()
+        b.record(main)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms_split = timed(split)
+    out_split = out.clone()
+    ms_stream = timed(streamed)
+    d = (out.float() - out_split.float()).abs().max().item()
+    return dict(ms_split=ms_split, ms_stream=ms_stream, kv_bytes=2 * C * chunk_bytes,
+                split_vs_streamed_max_abs=d)
+
+
+def burst_line(w, args):
+    n_split = 16
+    r = run_burst(w, args.steps, args.warmup, n_split)
+    flops = w.visible_pairs() * 4 * w.D
+    kv = r["kv_bytes"]
+    line = {
+        "metric": "Mode B burst verification TFLOP/s (64 queries x 1M Q8_0 keys, no causal mask)",
+        "value": round(flops / (r["ms_split"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_split"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=1 H=%d M=%d N=%d d=64 non-causal, Q8_0 KV resident in HBM "
+                               "split into %d key ranges held as the sequences of one state "
+                               "(chunks of %d tokens), merged pairwise with attn_state_merge; "
+                               "step = init + %d chunk calls + %d merges + finalize" % (
+                                   w.name, w.H, w.M, w.N, n_split, w.chunk,
+                                   w.n_chunks // n_split, n_split.bit_length() - 1)},
+        "kv_gbps_resident": round(kv / (r["ms_split"] * 1e-3) / 1e9, 2),
+        "fraction_of_mfma_peak": round(flops / (r["ms_split"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+                                       4),
+        "ms_streamed_one_state": round(r["ms_stream"], 4),
+        "kv_gbps_streamed": round(kv / (r["ms_stream"] * 1e-3) / 1e9, 3),
+        "split_vs_streamed_output_max_abs": r["split_vs_streamed_max_abs"],
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_streamed(w, steps, warmup):
     """The 1M-token workload: Q8_0 K and V in pinned host memory, chunk-major, streamed through
     two device slots per tensor by attn_accumulate_stream (copies on a side stream, compute on
@@ -174,19 +302,7 @@ def run_streamed(w, steps, warmup):
     dev = torch.device("cuda:0")
     H, C, chunk = w.H, w.n_chunks, w.chunk
     row = q8a.ROW_BYTES[q8a.KV_Q8_0]
-    kh = torch.empty((C, 1, H, chunk, row), dtype=torch.uint8, pin_memory=True)
-    vh = torch.empty(kh.shape, dtype=torch.uint8, pin_memory=True)
-    kd = torch.empty(kh.shape, dtype=torch.uint8, device=dev)  # resident copy (compute only)
-    vd = torch.empty_like(kd)
-    for c in range(C):  # draw and pack chunk by chunk (the FP32 cache never exists whole)
-        k, v = synthetic.gen_kv_chunk(w, c)
-        n = k.shape[1]
-        q8a.q8_0_pack(torch.from_numpy(k).to(dev), kd[c, 0, :, :n], H * n, w.D)
-        q8a.q8_0_pack(torch.from_numpy(v).to(dev), vd[c, 0, :, :n], H * n, w.D)
-        kh[c].copy_(kd[c])
-        vh[c].copy_(vd[c])
-        if c % 16 == 15:
-            print("packed chunk %d of %d" % (c + 1, C), file=sys.stderr, flush=True)
+    kd, vd, kh, vh = build_streamed_cache(w)
     qd = torch.from_numpy(synthetic.gen_q(w)).view(torch.float16).to(dev)
     m, l, o = q8a.alloc_state(1, H, w.M, dev)
     out = torch.empty((1, H, w.M, w.D), dtype=torch.float16, device=dev)
@@ -420,7 +536,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2,
-                    help="0-3: resident workloads; 4: the streamed 1M-token workload")
+                    help="0-3: resident workloads; 4: the streamed 1M-token workload; "
+                         "5: Mode B burst verification over the 1M-token cache")
     ap.add_argument("--chunk", type=int, default=None, help="override B_C")
     ap.add_argument("--kv", choices=["q8_0", "f16"], default="q8_0")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -456,6 +573,9 @@ def main():
     import chunked_flashattention_q8_amd as q8a
 
     w = synthetic.WORKLOADS[args.workload]
+    if w.streamed and not w.causal:
+        burst_line(w, args)
+        return
     if w.streamed:
         streamed_line(w, args)
         return

@@ -35,7 +35,8 @@ HEAD_DIM = 64
 ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
 
 EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_finalize",
-           "attn_accumulate_stream", "q8a_status_string", "q8a_last_hip_error")
+           "attn_state_merge", "attn_accumulate_stream", "q8a_status_string",
+           "q8a_last_hip_error")
 
 
 class Q8AError(RuntimeError):
@@ -75,6 +76,7 @@ def library() -> ctypes.CDLL:
     lib.attn_state_init.argtypes = [SP, P, P, P, i32, i32, i32, i32, i64, P]
     lib.attn_accumulate_chunk.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P]
     lib.attn_finalize.argtypes = [SP, P, P, P]
+    lib.attn_state_merge.argtypes = [SP, SP, P]
     lib.attn_accumulate_stream.argtypes = [SP, P, P, P, i32, i64, i32, ctypes.POINTER(P),
                                            ctypes.POINTER(P), i32, P, P]
     lib.q8a_status_string.restype = ctypes.c_char_p
@@ -82,7 +84,7 @@ def library() -> ctypes.CDLL:
     lib.q8a_last_hip_error.restype = ctypes.c_int
     lib.q8a_last_hip_error.argtypes = []
     for name in ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_finalize",
-                 "attn_accumulate_stream"):
+                 "attn_state_merge", "attn_accumulate_stream"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -143,6 +145,11 @@ def attn_finalize(st: q8a_state, out, lse=None, stream=None) -> None:
     _check(library().attn_finalize(ctypes.byref(st), _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def attn_state_merge(dst: q8a_state, src: q8a_state, stream=None) -> None:
+    """Merge partial state src (a disjoint key set, same rows) into dst."""
+    _check(library().attn_state_merge(ctypes.byref(dst), ctypes.byref(src), _stream(stream)))
+
+
 def attn_accumulate_stream(st: q8a_state, q, k_host, v_host, kv_dtype: int, n_kv_total: int,
                            chunk_tokens: int, slot_k, slot_v, causal: int = 1,
                            compute_stream=None, copy_stream=None) -> None:
@@ -153,6 +160,20 @@ def attn_accumulate_stream(st: q8a_state, q, k_host, v_host, kv_dtype: int, n_kv
                                             _ptr(v_host), int(kv_dtype), int(n_kv_total),
                                             int(chunk_tokens), sk, sv, int(causal),
                                             _stream(compute_stream), _stream(copy_stream)))
+
+
+def sub_state(st: q8a_state, s0: int, n: int) -> q8a_state:
+    """Descriptor of sequences [s0, s0 + n) of an initialised state (same buffers)."""
+    if not (0 <= s0 and n >= 1 and s0 + n <= st.n_seq):
+        raise ValueError("sequence range outside the state")
+    sub = q8a_state()
+    ctypes.memmove(ctypes.byref(sub), ctypes.byref(st), ctypes.sizeof(q8a_state))
+    rows = s0 * st.n_heads * st.n_q
+    sub.m = st.m + 4 * rows
+    sub.l = st.l + 4 * rows
+    sub.o = st.o + 4 * HEAD_DIM * rows
+    sub.n_seq = n
+    return sub
 
 
 def alloc_state(n_seq: int, n_heads: int, n_q: int, device="cuda"):

@@ -188,6 +188,35 @@ int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream)
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
+int attn_state_merge(const q8a_state *dst, const q8a_state *src, void *stream)
+{
+    int rc = check_state(dst);
+    if (rc)
+        return rc;
+    rc = check_state(src);
+    if (rc)
+        return rc;
+    if (dst->n_seq != src->n_seq || dst->n_heads != src->n_heads || dst->n_q != src->n_q ||
+        dst->q_pos0 != src->q_pos0)
+        return Q8A_E_STATE;
+    const int64_t rows = state_rows(dst);
+    // the two states must not share memory (a state merged with itself would count its keys
+    // twice; overlapping buffers would race)
+    auto overlap = [](const void *a, int64_t na, const void *b, int64_t nb) {
+        const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+        return x < y + nb && y < x + na;
+    };
+    const float *dm[3] = {dst->m, dst->l, dst->o}, *sm[3] = {src->m, src->l, src->o};
+    const int64_t bytes[3] = {rows * 4, rows * 4, rows * 4 * q8a::kHeadDim};
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            if (overlap(dm[i], bytes[i], sm[j], bytes[j]))
+                return Q8A_E_INVAL;
+    hipError_t e = q8a::launch_merge(dst->m, dst->l, dst->o, src->m, src->l, src->o, rows,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
 int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_host,
                            const void *v_host, int32_t kv_dtype, int64_t n_kv_total,
                            int32_t chunk_tokens, void *const slot_k[2], void *const slot_v[2],

@@ -616,6 +616,53 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__
     out[row * 8 + part] = res;
 }
 
+// Merge partial state b into partial state a, row by row: m' = max(m_a, m_b), then l and O of
+// each side are rescaled by e^(m - m') and added (the chunk rescale of "Out-of-Core Flash
+// Streaming & Speculative Decode (1M Context)", Sec. 3, with b's summary in the chunk's place).
+// An empty b (m = -inf) leaves a untouched; an empty a takes b.  Eight lanes per row, eight O
+// values each; all lanes of a row read its m and l before lane 0 writes them.
+__global__ __launch_bounds__(256) void merge_kernel(float *__restrict__ ma, float *__restrict__ la,
+                                                    float4 *__restrict__ oa,
+                                                    const float *__restrict__ mb,
+                                                    const float *__restrict__ lb,
+                                                    const float4 *__restrict__ ob,
+                                                    int64_t n_rows)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid >> 3;
+    const int part = (int)(gid & 7);
+    if (row >= n_rows)
+        return;
+    const float m2 = mb[row];
+    if (m2 == -INFINITY)
+        return;
+    const float m1 = ma[row];
+    const float4 y0 = ob[row * 16 + 2 * part], y1 = ob[row * 16 + 2 * part + 1];
+    float4 r0, r1;
+    float mn, ln;
+    if (m1 == -INFINITY) {
+        r0 = y0;
+        r1 = y1;
+        mn = m2;
+        ln = lb[row];
+    } else {
+        mn = fmaxf(m1, m2);
+        const float fa = expf(m1 - mn), fb = expf(m2 - mn);
+        const float4 x0 = oa[row * 16 + 2 * part], x1 = oa[row * 16 + 2 * part + 1];
+        r0 = make_float4(x0.x * fa + y0.x * fb, x0.y * fa + y0.y * fb, x0.z * fa + y0.z * fb,
+                         x0.w * fa + y0.w * fb);
+        r1 = make_float4(x1.x * fa + y1.x * fb, x1.y * fa + y1.y * fb, x1.z * fa + y1.z * fb,
+                         x1.w * fa + y1.w * fb);
+        ln = la[row] * fa + lb[row] * fb;
+    }
+    oa[row * 16 + 2 * part] = r0;
+    oa[row * 16 + 2 * part + 1] = r1;
+    if (part == 0) {
+        ma[row] = mn;
+        la[row] = ln;
+    }
+}
+
 } // namespace
 
 hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s)
@@ -632,6 +679,16 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
         hipLaunchKernelGGL(accumulate_kernel<0>, grid, dim3(NTHR), 0, s, a);
     else
         hipLaunchKernelGGL(accumulate_kernel<1>, grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(float *ma, float *la, float *oa, const float *mb, const float *lb,
+                        const float *ob, int64_t n_rows, hipStream_t s)
+{
+    const int64_t grid = (n_rows * 8 + 255) / 256;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(256), 0, s, ma, la,
+                       reinterpret_cast<float4 *>(oa), mb, lb,
+                       reinterpret_cast<const float4 *>(ob), n_rows);
     return hipGetLastError();
 }
 

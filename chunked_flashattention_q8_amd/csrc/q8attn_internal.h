@@ -31,5 +31,7 @@ hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s);
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s);
 hipError_t launch_finalize(const float *m, const float *l, const float *o, void *out,
                            float *lse, int64_t n_rows, hipStream_t s);
+hipError_t launch_merge(float *ma, float *la, float *oa, const float *mb, const float *lb,
+                        const float *ob, int64_t n_rows, hipStream_t s);
 
 } // namespace q8a

@@ -54,7 +54,10 @@ typedef enum {
 
 /* Host-side descriptor of a caller-owned online-softmax state.  Filled by attn_state_init; the
  * other calls only read it.  A state row whose m is -inf is EMPTY: it has seen no key, its l is 0
- * and its O is treated as zero and never read (so O need not be cleared). */
+ * and its O is treated as zero and never read (so O need not be cleared).
+ * A descriptor of sequences [s0, s0 + n) of an initialised state is a copy of its descriptor
+ * with m and l advanced by s0*n_heads*n_q floats, o by 64 times that, and n_seq = n; it may be
+ * passed wherever a state is (for example to merge sequence blocks of one state). */
 typedef struct {
     float *m;          /* [n_seq][n_heads][n_q]      running maximum of the scaled logits  */
     float *l;          /* [n_seq][n_heads][n_q]      running sum of e^(S - m)             */
@@ -111,6 +114,21 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
  * lse = -inf.  out: FP16 [n_seq][n_heads][n_q][64], 16-byte aligned; lse: FP32 [..][n_q] or NULL.
  * The state is not modified. */
 int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream);
+
+/* Merge the partial state src into dst.  Each must hold, for the same rows, the accumulation of
+ * a key set, the two key sets disjoint; afterwards dst holds what accumulating both key sets
+ * into one state gives (up to rounding): m = max(m_dst, m_src), and l and O of each side
+ * rescaled by e^(m_side - m) and added -- the chunk rescale of "Out-of-Core ...", Sec. 3, with
+ * src's (m, l, O) in the chunk's place.  Rows empty in src leave dst untouched; rows empty in
+ * dst take src's values.  With it a key range can be split over several states that
+ * accumulate concurrently (for example on several streams when few query rows leave the GPU
+ * idle, as in Mode B of "Out-of-Core ...", Sec. 4) and merged afterwards; the same rule merges
+ * states built on different devices.
+ *   dst, src  initialised states with equal n_seq, n_heads, n_q and q_pos0 (else Q8A_E_STATE),
+ *             whose buffers do not overlap (else Q8A_E_INVAL).  src is not modified.
+ * Both states must be stream-ordered before the call (dst and src work on `stream` or
+ * synchronised with it). */
+int attn_state_merge(const q8a_state *dst, const q8a_state *src, void *stream);
 
 /* Double-buffered streaming of a KV cache held in pinned host memory ("Out-of-Core ...", Sec. 2:
  * two ping-pong slots, chunk c+1 copied while chunk c is computed, handoff by synchronisation

@@ -15,7 +15,12 @@ id    name                B   H   M      N          q_pos0     B_C      checked
 2     batch8_m2048        8   32  2048   2048       0          512      sampled
 3     append_133k         1   32  2048   133120     131072     8192     64/head
 4     stream_1m           1   32  2048   1048576    1046528    16384    32/head
+5     burst_verify_1m     1   32  64     1048576    1048576    16384    all rows
 ====  ==================  ==  ==  =====  =========  =========  =======  =========
+
+Workload 5 is Mode B of "Out-of-Core Flash Streaming & Speculative Decode (1M Context)", Sec. 4:
+64 candidate queries (positions just past the cache) attend to the whole 1M-token context with
+no causal mask.
 
 Draws: every tensor is a stack of [rows, 64] slices, one per (sequence, head); slice i of a
 tensor with seed s is filled by ``torch.Tensor.normal_`` (float32, mean 0, std 1) from its own
@@ -52,6 +57,7 @@ class Workload:
     chunk: int
     rows_per_head: int | None  # None = every row is checked
     streamed: bool = False
+    causal: bool = True
 
     @property
     def D(self) -> int:
@@ -67,7 +73,10 @@ class Workload:
                 for c in range(self.n_chunks)]
 
     def visible_pairs(self) -> int:
-        """Number of (query, key) pairs with key position <= query position, over all heads."""
+        """Number of visible (query, key) pairs over all heads: key position <= query position
+        when causal, every pair otherwise."""
+        if not self.causal:
+            return self.M * self.N * self.B * self.H
         pos = self.q_pos0 + np.arange(self.M, dtype=np.int64)
         per_head = int(np.minimum(pos + 1, self.N).sum())
         return per_head * self.B * self.H
@@ -79,6 +88,8 @@ WORKLOADS = {
     2: Workload(2, "batch8_m2048", 8, 32, 2048, 2048, 0, 512, 16),
     3: Workload(3, "append_133k", 1, 32, 2048, 133120, 131072, 8192, 64),
     4: Workload(4, "stream_1m", 1, 32, 2048, 1048576, 1046528, 16384, 32, streamed=True),
+    5: Workload(5, "burst_verify_1m", 1, 32, 64, 1048576, 1048576, 16384, None, streamed=True,
+                causal=False),
 }
 
 

@@ -129,6 +129,27 @@ def test_finalize_rejects_bad_arguments():
     assert lib.attn_finalize(ctypes.byref(st), P(A16), P(A16B + 1), None) == q8a.Q8A_E_ALIGN
 
 
+def test_merge_rejects_bad_arguments():
+    lib = q8a.library()
+
+    def merge(a, b):
+        return lib.attn_state_merge(ctypes.byref(a), ctypes.byref(b), None)
+    a = fake_state()
+    b = fake_state()
+    b.m, b.l, b.o = 0x110000, 0x120000, 0x200000
+    assert merge(q8a.q8a_state(), b) == q8a.Q8A_E_STATE       # dst not initialised
+    assert merge(a, q8a.q8a_state()) == q8a.Q8A_E_STATE       # src not initialised
+    for field, value in (("n_q", 128), ("n_heads", 2), ("n_seq", 2), ("q_pos0", 5)):
+        c = fake_state()
+        c.m, c.l, c.o = b.m, b.l, b.o
+        setattr(c, field, value)
+        assert merge(a, c) == q8a.Q8A_E_STATE, field
+    assert merge(a, a) == q8a.Q8A_E_INVAL                     # a state with itself
+    c = fake_state()
+    c.m, c.l, c.o = b.m, b.l, A16C + 64                       # O buffers overlap
+    assert merge(a, c) == q8a.Q8A_E_INVAL
+
+
 def test_stream_rejects_bad_arguments():
     lib = q8a.library()
     P = ctypes.c_void_p
