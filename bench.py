@@ -149,10 +149,29 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
         if pairs:
             d = [a.elapsed_time(b) for a, b in pairs]
             kern[key] = {"launches_per_step": len(d) // steps, "mean_us": 1e3 * float(np.mean(d))}
+    # the same step captured once into a HIP graph and replayed: a secondary, labelled number
+    # (fewer launch gaps); every replay must reproduce the eager output bit for bit
+    ref_out, ref_lse = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(False)
+    out.zero_()
+    lse.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_equal = bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse))
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / steps
+    graph_equal = graph_equal and bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse))
     acc_ms = [a.elapsed_time(b) for a, b in ev["accumulate"]]
     acc_mean_ms = float(np.mean(acc_ms))
     acc_flops_mean = float(np.mean(acc_flops))
     res = dict(q=q, out=out, lse=lse, ms_clean=ms_clean, ms_events=ms_events, kernels=kern,
+               ms_graph=ms_graph, graph_equal=graph_equal,
                acc_mean_ms=acc_mean_ms, acc_flops_mean=acc_flops_mean,
                acc_per_chunk_us=[1e3 * float(np.mean(acc_ms[i::len(chunks)]))
                                  for i in range(len(chunks))],
@@ -623,6 +642,10 @@ def main():
         "step_fraction_of_mfma_peak": round(value / PEAK_F16_TFLOPS, 4),
         "kv_gbps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
         "ms_per_step_with_kernel_events": round(res["ms_events"], 5),
+        "hip_graph": {"ms_per_step": round(res["ms_graph"], 5),
+                      "value": round(flops_step / (res["ms_graph"] * 1e-3) / 1e12, 3),
+                      "output_equals_eager": res["graph_equal"],
+                      "note": "the same step captured once with torch.cuda.graph and replayed"},
         "kernels": res["kernels"],
         "accumulate_us_per_chunk": [round(x, 3) for x in res["acc_per_chunk_us"]],
     }

@@ -3,9 +3,10 @@
 //
 // HBM-bound: each 32-value block reads 128 bytes and writes 34.  Eight consecutive lanes own one
 // block and each loads one 16-byte float4, so a wavefront reads 1 KiB of contiguous input per
-// instruction; every lane handles two blocks, 256 float4 apart, with both loads in flight.  The block's largest magnitude is reduced over the eight lanes, every lane derives
-// the same FP16 scale, quantises its four values and writes them as two 16-bit stores (block
-// starts are 2-byte aligned: 34 * k).
+// instruction; every lane handles two blocks, 256 float4 apart, with both loads in flight.  The
+// block's largest magnitude is reduced over the eight lanes, every lane derives the same FP16
+// scale, quantises its four values and writes them as two 16-bit stores (block starts are 2-byte
+// aligned: 34 * k).
 //
 // Arithmetic (bit-exact with the CPU oracle): d = amax / 127 with a correctly rounded FP32
 // division; d16 = FP16(d), round to nearest even; q = round(x / d16) with a correctly rounded
