@@ -9,9 +9,9 @@
 // ("Core Architecture & The 4-Brick Pipeline", Sec. 5).
 //
 // Accumulate kernel, one workgroup = 4 wavefronts = 256 query rows of one (sequence, head):
-//   * K/V tiles of 64 keys are fetched with 128-bit buffer loads (bytes past the chunk read as
-//     0) two tiles ahead into registers, staged in LDS as raw Q8_0 rows, then unpacked in LDS
-//     into a double-buffered operand tile (one barrier per tile):
+//   * K/V tiles of 64 keys are copied as raw rows straight from HBM into LDS two tiles ahead
+//     (128-bit buffer loads that write LDS directly; bytes past the chunk read as 0), then
+//     unpacked in LDS into a double-buffered operand tile (one barrier per tile):
 //       - K: the exact int8 values times the FP16 scale, split into two FP16 halves
 //         hi = fp16(q*d) and lo = q*d - hi (exact, q*d has at most 18 significant bits), so
 //         Q.K^T on FP16 MFMA reproduces the dequantised logits up to FP32 accumulation;
@@ -42,6 +42,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int QT = 256;  // query rows per workgroup (4 wavefronts x 2 blocks of 32)
 constexpr int WQ = 32;   // query rows per MFMA block
@@ -362,12 +363,13 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     const uint32_t head_bytes = ((uint32_t)a.n_kv * ROW + 15u) & ~15u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, head_bytes);
-    // Prefetch slots: each slot is one 16-byte piece of the K or the V tile, and within a
-    // wavefront a slot always belongs to the same tensor (buffer resources must be uniform).
+    // Raw rows are copied HBM -> LDS by buffer loads that write LDS directly (no registers, no
+    // LDS store instructions): one instruction moves 16 bytes per lane to base + 16 * lane, so
+    // each slot below covers 64 consecutive 16-byte pieces of one tensor per wavefront (the
+    // buffer resource and the LDS base must be wavefront-uniform).
     //   Q8_0 (272 pieces per tensor): slot 0 = K piece tid, slot 1 = V piece tid, slot 2 = the
     //   16 remaining K pieces on wavefront 0 and the 16 remaining V pieces on wavefront 1.
     //   FP16 (512 pieces per tensor): slots 0, 1 = K pieces tid, tid + 256; slots 2, 3 = V.
-    u32x4 pre[NPRE];
     auto slot = [&](int sl, int &tensor, int &piece) -> bool {
         if constexpr (FMT == 0) {
             if (sl < 2) {
@@ -384,41 +386,32 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             return true;
         }
     };
-    auto fetch = [&](int t, u32x4 (&dst)[NPRE]) {
+    // raw rows of tile t into raw buffer buf; complete once vmcnt reaches 0
+    auto fetch = [&](int t, int buf) {
 #pragma unroll
         for (int sl = 0; sl < NPRE; ++sl) {
             int tensor, piece;
             if (slot(sl, tensor, piece)) {
                 const uint32_t off = (uint32_t)t * (KT * ROW) + 16u * piece;
-                dst[sl] = load16(tensor ? rv : rk, off);
+                uint8_t *dst = &sm.raw[buf][tensor][16 * (piece - lane)];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor ? rv : rk, (lds_void *)dst, 16, off,
+                                                         0, 0, 0);
             }
-        }
-    };
-    auto stash = [&](int buf, const u32x4 (&src)[NPRE]) {
-#pragma unroll
-        for (int sl = 0; sl < NPRE; ++sl) {
-            int tensor, piece;
-            if (slot(sl, tensor, piece))
-                *reinterpret_cast<u32x4 *>(&sm.raw[buf][tensor][16 * piece]) = src[sl];
         }
     };
 
     // Loads past the chunk read as zero, and operand tiles unpacked from raw rows past the last
-    // tile are never read, so fetch / stash / unpack run unconditionally (no branches inside
-    // the tile loop's scheduling regions).
-    {
-        u32x4 pre1[NPRE]; // both prologue tiles are in flight at once
-        fetch(0, pre);
-        fetch(1, pre1);
-        stash(0, pre);
-        stash(1, pre1);
-    }
+    // tile are never read, so fetch and unpack run unconditionally (no branches inside the
+    // tile loop's scheduling regions).
+    fetch(0, 0);
+    fetch(1, 1);
+    __builtin_amdgcn_s_waitcnt(0); // the copies have landed in LDS before the barrier
     __syncthreads();
     unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
     __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
-        fetch(t + 2, pre);
+        fetch(t + 2, t & 1); // raw buffer t&1 was unpacked in the previous interval
         const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
         // tile t+1 is unpacked from its raw rows in every branch: the same barrier interval
@@ -544,7 +537,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
         }
-        stash(t & 1, pre); // raw rows of tile t+2 (raw buffer t&1 was unpacked in the last interval)
+        __builtin_amdgcn_s_waitcnt(0); // raw rows of tile t+2 have landed before the barrier
         __syncthreads();
     }
 
