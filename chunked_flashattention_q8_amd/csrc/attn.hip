@@ -242,9 +242,16 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
     }
 }
 
-template <int FMT>
+// SPLIT (used when a workgroup's query rows fit in 64): instead of two 32-row blocks over all
+// keys, wavefront w owns block w & 1 over the keys of subtile w >> 1 (keys 32(w>>1) .. +31 of
+// every tile), with an online-softmax state of its own; the two states of a block are merged
+// through LDS at the end by the rule attn_state_merge uses.  All four wavefronts then work on
+// the 64 rows instead of two of them (each also carrying an empty block).
+template <int FMT, bool SPLIT>
 __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 {
+    constexpr int NJ = SPLIT ? 1 : 2; // 32-row query blocks per wavefront
+    constexpr int NS = SPLIT ? 1 : 2; // 32-key subtiles per wavefront and tile
     constexpr int ROW = Smem<FMT>::ROW;
     constexpr int RAW16 = KT * ROW / 16;                 // 16-byte pieces per tensor tile
     constexpr int NPRE = FMT == 0 ? 3 : 4;               // prefetch slots per thread
@@ -256,6 +263,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: keep it scalar
     const int qcol = lane & 31, g = lane >> 5;
+    const int kh = SPLIT ? (wave >> 1) : 0; // SPLIT: this wavefront's key subtile
 
     // ---- workgroup -> (sequence, head, query tile).  Workgroups are dispatched round-robin over
     // the 8 XCDs; each XCD gets a contiguous set of heads (their K/V stay in its L2) and within
@@ -288,14 +296,14 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         return; // the whole workgroup sees nothing of this chunk
     const int n_tiles = (kv_end_wg + KT - 1) / KT;
 
-    // ---- this wavefront's two 32-row query blocks: w and 7 - w of the tile (balances the
-    // causal diagonal across wavefronts)
-    int kv_end_b[2], kv_full_b[2], qi[2], lim[2];
-    bool q_ok[2];
-    int64_t row[2];
+    // ---- this wavefront's 32-row query blocks: w and 7 - w of the tile (balances the causal
+    // diagonal across wavefronts); SPLIT: block w & 1
+    int kv_end_b[NJ], kv_full_b[NJ], qi[NJ], lim[NJ];
+    bool q_ok[NJ];
+    int64_t row[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int q0 = q_wg0 + WQ * (j == 0 ? wave : 7 - wave);
+    for (int j = 0; j < NJ; ++j) {
+        const int q0 = q_wg0 + WQ * (SPLIT ? (wave & 1) : (j == 0 ? wave : 7 - wave));
         const bool live = q0 < a.M;
         kv_end_b[j] = live ? kv_end_for(min(q0 + WQ, a.M) - 1) : 0;
         kv_full_b[j] = (q0 + WQ <= a.M) ? kv_end_for(q0) : 0;
@@ -305,15 +313,19 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         lim[j] = q_ok[j] ? kv_end_for(qi[j]) - 1 : -1;
         row[j] = head * a.M + qi[j];
     }
-    const int kv_end_w = max(kv_end_b[0], kv_end_b[1]);
-    const int kv_full_w = min(kv_full_b[0], kv_full_b[1]); // keys every row of the wave sees
-
-    half8 qreg[2][4];
-    floatx16 o[2][2];
-    float l_part[2], m_raw[2], m_ref[2];
-    bool saw[2];
+    int kv_end_w = kv_end_b[0], kv_full_w = kv_full_b[0]; // kv_full_w: keys all rows see
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 1; j < NJ; ++j) {
+        kv_end_w = max(kv_end_w, kv_end_b[j]);
+        kv_full_w = min(kv_full_w, kv_full_b[j]);
+    }
+
+    half8 qreg[NJ][4];
+    floatx16 o[NJ][2];
+    float l_part[NJ], m_raw[NJ], m_ref[NJ];
+    bool saw[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             o[j][0][v] = 0.f;
@@ -329,8 +341,10 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 qreg[j][kk] = qrow[2 * kk + g];
-            const float mo = a.m[row[j]];
-            if (mo != -INFINITY) { // non-empty row: resume from its state
+            // non-empty row: resume from its state (SPLIT: in the first key subtile's
+            // wavefront only; the other starts empty and is merged in at the end)
+            const float mo = (!SPLIT || kh == 0) ? a.m[row[j]] : -INFINITY;
+            if (mo != -INFINITY) {
                 m_raw[j] = mo * 8.0f;
                 m_ref[j] = m_raw[j] * kScaleLog2;
                 if (g == 0)
@@ -418,31 +432,33 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         // that reads operand buffer t&1 writes buffer (t+1)&1
         if (key0 < kv_end_w) {
             // S^T = K Q^T: lane (qcol, g) holds
-            // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][sub][v]
-            floatx16 s[2][2];
+            // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][si][v], sub the
+            // si-th key subtile this wavefront covers
+            floatx16 s[NJ][NS];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
+                for (int si = 0; si < NS; ++si)
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        s[j][sub][v] = 0.f;
+                        s[j][si][v] = 0.f;
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
+            for (int si = 0; si < NS; ++si) {
+                const int sub = SPLIT ? kh : si;
                 const int kr = (32 * sub + qcol) * KP + 8 * g;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[j][kk],
-                                                                          s[j][sub], 0, 0, 0);
+                    for (int j = 0; j < NJ; ++j)
+                        s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[j][kk],
+                                                                         s[j][si], 0, 0, 0);
                     if constexpr (FMT == 0) {
                         const half8 al = *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
 #pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            s[j][sub] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                al, qreg[j][kk], s[j][sub], 0, 0, 0);
+                        for (int j = 0; j < NJ; ++j)
+                            s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                al, qreg[j][kk], s[j][si], 0, 0, 0);
                     }
                 }
             }
@@ -455,31 +471,42 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             // skips this with one wavefront-uniform test.
             if (key0 + KT > kv_full_w) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
                     const int rel = lim[j] - key0 - 4 * g;
 #pragma unroll
-                    for (int sub = 0; sub < 2; ++sub)
+                    for (int si = 0; si < NS; ++si) {
+                        const int sub = SPLIT ? kh : si;
                         if (key0 + 32 * sub + 32 > kv_full_b[j]) {
 #pragma unroll
                             for (int v = 0; v < 16; ++v)
-                                s[j][sub][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
-                                                   ? s[j][sub][v] : -INFINITY;
+                                s[j][si][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
+                                                  ? s[j][si][v] : -INFINITY;
                         }
+                    }
                 }
             }
             bool need_any = false;
-            float mx2[2];
+            float mx2[NJ];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
-                float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
+            for (int j = 0; j < NJ; ++j) {
+                float mx;
+                if constexpr (NS == 2) {
+                    float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
+                    float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
 #pragma unroll
-                for (int v = 3; v < 15; v += 2) {
-                    ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
-                    mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
+                    for (int v = 3; v < 15; v += 2) {
+                        ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
+                        mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
+                    }
+                    mx = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
+                } else {
+                    float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
+#pragma unroll
+                    for (int v = 3; v < 15; v += 2)
+                        ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
+                    mx = fmaxf(ma, s[j][0][15]);
                 }
-                float mx = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
                 mx = half_swap_max(mx);
                 m_raw[j] = fmaxf(m_raw[j], mx);
                 saw[j] = saw[j] || (mx != -INFINITY);
@@ -488,7 +515,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             }
             if (__builtin_amdgcn_ballot_w64(need_any)) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
                     const float alpha = (m_ref[j] == -INFINITY)
                                             ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
@@ -501,35 +528,36 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             // per query block: P = exp2(S*log2e/8 - ref) (l sums the FP32 values), P to FP16,
             // then O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
                 float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
-                half8 p16[2][2];
+                half8 p16[NS][2];
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
+                for (int si = 0; si < NS; ++si) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const float p = __builtin_amdgcn_exp2f(
-                            __builtin_fmaf(s[j][sub][v], kScaleLog2, -base));
-                        s[j][sub][v] = p;
+                            __builtin_fmaf(s[j][si][v], kScaleLog2, -base));
+                        s[j][si][v] = p;
                         ls[v & 3] += p;
                     }
-                    p16[sub][0] = to_half8(s[j][sub], 0);
-                    p16[sub][1] = to_half8(s[j][sub], 8);
+                    p16[si][0] = to_half8(s[j][si], 0);
+                    p16[si][1] = to_half8(s[j][si], 8);
                 }
                 l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
                 // the V tile's key order matches the accumulator layout
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
+                for (int si = 0; si < NS; ++si)
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
+                        const int sub = SPLIT ? kh : si;
                         const int pos = 32 * sub + 16 * tt + 8 * g;
                         const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
                         const half8 a1 =
                             *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
-                        o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p16[sub][tt],
+                        o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p16[si][tt],
                                                                          o[j][0], 0, 0, 0);
-                        o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p16[sub][tt],
+                        o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p16[si][tt],
                                                                          o[j][1], 0, 0, 0);
                     }
             }
@@ -541,10 +569,48 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         __syncthreads();
     }
 
+    if constexpr (SPLIT) {
+        // merge the two key subtiles' states of each block: the second subtile's wavefront
+        // (kh = 1) leaves its per-lane state in LDS (the loop's last barrier has retired every
+        // use of the tile buffers), the first (kh = 0, same lanes, same block) folds it in
+        static_assert(sizeof(Smem<FMT>) >= 2 * 64 * 36 * sizeof(float), "merge area");
+        float *xb = reinterpret_cast<float *>(&sm) + ((wave & 1) * 64 + lane) * 36;
+        if (kh == 1) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                xb[v] = o[0][0][v];
+                xb[16 + v] = o[0][1][v];
+            }
+            xb[32] = l_part[0];
+            xb[33] = m_ref[0];
+            xb[34] = m_raw[0];
+            xb[35] = saw[0] ? 1.f : 0.f;
+        }
+        __syncthreads();
+        if (kh == 0) {
+            const float mb = xb[33];
+            if (mb != -INFINITY) { // the other subtile's state is not empty
+                const float ma = m_ref[0];
+                const float mn = fmaxf(ma, mb);
+                const float fa = (ma == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ma - mn);
+                const float fb = __builtin_amdgcn_exp2f(mb - mn);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    o[0][0][v] = o[0][0][v] * fa + xb[v] * fb;
+                    o[0][1][v] = o[0][1][v] * fa + xb[16 + v] * fb;
+                }
+                l_part[0] = l_part[0] * fa + xb[32] * fb;
+                m_ref[0] = mn;
+            }
+            m_raw[0] = fmaxf(m_raw[0], xb[34]);
+            saw[0] = saw[0] || xb[35] != 0.f;
+        }
+    }
+
     // ---- write back the rows that saw at least one key, renormalised to the true maximum
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        if (kv_end_b[j] > 0) { // uniform per wavefront
+    for (int j = 0; j < NJ; ++j) {
+        if (kv_end_b[j] > 0 && (!SPLIT || kh == 0)) { // uniform per wavefront
             const float l_tot = half_swap_sum(l_part[j]);
             if (q_ok[j] && saw[j]) {
                 const float rr = __builtin_amdgcn_exp2f(m_ref[j] - m_raw[j] * kScaleLog2);
@@ -668,10 +734,19 @@ hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s)
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s)
 {
     const dim3 grid((unsigned)(((a.M + QT - 1) / QT) * a.B * a.H));
-    if (kv_dtype == 0)
-        hipLaunchKernelGGL(accumulate_kernel<0>, grid, dim3(NTHR), 0, s, a);
-    else
-        hipLaunchKernelGGL(accumulate_kernel<1>, grid, dim3(NTHR), 0, s, a);
+    // up to 64 query rows (two blocks): split the keys of every tile between wavefront pairs
+    const bool split = a.M <= 2 * WQ;
+    if (kv_dtype == 0) {
+        if (split)
+            hipLaunchKernelGGL((accumulate_kernel<0, true>), grid, dim3(NTHR), 0, s, a);
+        else
+            hipLaunchKernelGGL((accumulate_kernel<0, false>), grid, dim3(NTHR), 0, s, a);
+    } else {
+        if (split)
+            hipLaunchKernelGGL((accumulate_kernel<1, true>), grid, dim3(NTHR), 0, s, a);
+        else
+            hipLaunchKernelGGL((accumulate_kernel<1, false>), grid, dim3(NTHR), 0, s, a);
+    }
     return hipGetLastError();
 }
 

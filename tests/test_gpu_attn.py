@@ -46,6 +46,10 @@ CASES = [
     (1, 2, 100, 152, 0, 52, 0),       # non-causal
     (1, 2, 40, 500, 0, 128, 1),       # chunks after every query position: no row touched
     (3, 1, 384, 384, 0, 384, 1),      # three sequences, full diagonal in one chunk
+    # up to 64 rows: the keys of every tile are split between wavefront pairs
+    (2, 2, 33, 290, 257, 64, 1),      # second 32-row block holds one row
+    (1, 3, 64, 640, 0, 160, 0),       # non-causal, state resumed over four chunks
+    (2, 1, 57, 1200, 1150, 300, 1),   # diagonal in the last chunk, ragged last tile
 ]
 
 
@@ -64,9 +68,10 @@ def test_small_cases(orc, case):
                  O_ref, lse_ref, str(case))
 
 
-def test_fp16_kv_small(orc):
-    B, H, M, N, q_pos0 = 2, 2, 150, 260, 110
-    say("fp16 kv")
+@pytest.mark.parametrize("M", [150, 50])
+def test_fp16_kv_small(orc, M):
+    B, H, N, q_pos0 = 2, 2, 260, 110
+    say("fp16 kv, M", M)
     prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=77, kv_dtype=q8a.KV_F16)
     out, lse, _ = prefill(qd, kd, vd, q8a.KV_F16, B, H, M, N, q_pos0, chunk_list(N, 80))
     O_ref, lse_ref = orc.attention(prob)
