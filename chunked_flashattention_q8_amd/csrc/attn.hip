@@ -12,9 +12,11 @@
 //   * K/V tiles of 64 keys are copied as raw rows straight from HBM into LDS two tiles ahead
 //     (128-bit buffer loads that write LDS directly; bytes past the chunk read as 0), then
 //     unpacked in LDS into a double-buffered operand tile (one barrier per tile):
-//       - K: the exact int8 values times the FP16 scale, split into two FP16 halves
-//         hi = fp16(q*d) and lo = q*d - hi (exact, q*d has at most 18 significant bits), so
-//         Q.K^T on FP16 MFMA reproduces the dequantised logits up to FP32 accumulation;
+//       - K: the int8 values q as FP16 (exact), plus two FP32 factors per key built from its
+//         block scales d0, d1: the MFMAs over dims 0-31 give S0 = Q.q0, the accumulator is
+//         multiplied by d0/d1, the MFMAs over dims 32-63 add S1 = Q.q1, and one FMA with
+//         d1*log2(e)/8 yields the base-2 exponent -- the dequantised logit d0 S0 + d1 S1 up to
+//         FP32 rounding, with no FP16 rounding of the dequantised K;
 //       - V: fp16(q*d), transposed to [dim][key] (one rounding of the dequantised value).
 //   * Each wavefront owns two 32-row query blocks (w and 7 - w of the tile, which balances the
 //     causal diagonal) and computes S^T = K Q^T with v_mfma_f32_32x32x16_f16, so each lane
@@ -50,7 +52,9 @@ constexpr int KT = 64;   // keys per LDS tile
 constexpr int NTHR = 256;
 constexpr int KP = 72;   // LDS pitch (halves) of the K tiles (144-byte rows)
 constexpr int VP = 72;   // LDS pitch (halves) of the transposed V tile
-constexpr float kScaleLog2 = 0.125f * 1.44269504088896340736f; // 1/sqrt(64) * log2(e)
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kScaleLog2 = 0.125f * kLog2e; // 1/sqrt(64) * log2(e)
 constexpr float kTau = 8.0f; // lazy rescale threshold, log2 units
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
@@ -122,9 +126,13 @@ __device__ __forceinline__ float half_swap_sum(float x)
 }
 
 template <int FMT> // 0: Q8_0 rows (68 bytes), 1: FP16 rows (128 bytes)
-struct KvTile {     // one LDS buffer of unpacked MFMA operands for KT keys
-    _Float16 khi[KT * KP];                     // K (Q8_0: fp16(q*d)), [key][dim]
-    _Float16 klo[FMT == 0 ? KT * KP : 8];      // Q8_0: q*d - khi, [key][dim]
+struct alignas(16) KvTile { // one LDS buffer of unpacked MFMA operands for KT keys
+    _Float16 k[KT * KP];                       // K (Q8_0: the int8 values q), [key][dim]
+    // Q8_0 logit scales of each key (block scales d0, d1): S = (S0 * kr + S1) * km / kScaleLog2
+    // with S0, S1 the products over the two blocks' q; kr = d0 / d1 and km = d1 * kScaleLog2
+    // (d1 = 0, where S1 = 0: kr = d0, km = kScaleLog2)
+    alignas(16) float kr[FMT == 0 ? KT : 4];
+    alignas(16) float km[FMT == 0 ? KT : 4];
     _Float16 vt[64 * VP];                      // V (Q8_0: fp16(q*d)), [dim][vpos]
 };
 
@@ -142,11 +150,10 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                                             int tid, int valid_keys)
 {
     if constexpr (FMT == 0) {
-        { // K: thread = (block, key, 16-value half); waves 0-1 block 0, waves 2-3 block 1.
-            // The 16 values sit at byte 34*blk + 2 + 16*hh of the row: read the 5 dwords that
-            // cover them and realign (by 2 bytes for block 0, none for block 1).  No branches,
-            // so this work can be scheduled among the matrix instructions.
-            const int blk = tid >> 7, key = (tid & 127) >> 1, hh = tid & 1;
+        { // K: thread = (key, quarter of the dims); quarter qq = dims 16qq .. 16qq+15, which
+            // sit at byte 34*blk + 2 + 16*hh of the row (blk = qq/2, hh = qq%2): read the 5 dwords
+            // that cover them and realign (by 2 bytes for block 0, none for block 1).
+            const int key = tid >> 2, qq = tid & 3, blk = qq >> 1, hh = qq & 1;
             const uint8_t *rr = rk + key * 68;
             const int off = 34 * blk + 2 + 16 * hh, sh = off & 3;
             const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + (off & ~3));
@@ -156,25 +163,30 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh);
             w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh);
             w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh);
-            const _Float16 d = *reinterpret_cast<const _Float16 *>(rr + 34 * blk);
-            const half2v d2 = {d, d};
-            half8 hi8[2], lo8[2];
+            half8 q8[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 half2v q01, q23;
                 i8x4_to_f16(w[i], q01, q23);
-                const half2v h01 = q01 * d2, h23 = q23 * d2;
-                const half2v l01 = __builtin_elementwise_fma(q01, d2, -h01);
-                const half2v l23 = __builtin_elementwise_fma(q23, d2, -h23);
-                hi8[i >> 1][4 * (i & 1) + 0] = h01[0]; hi8[i >> 1][4 * (i & 1) + 1] = h01[1];
-                hi8[i >> 1][4 * (i & 1) + 2] = h23[0]; hi8[i >> 1][4 * (i & 1) + 3] = h23[1];
-                lo8[i >> 1][4 * (i & 1) + 0] = l01[0]; lo8[i >> 1][4 * (i & 1) + 1] = l01[1];
-                lo8[i >> 1][4 * (i & 1) + 2] = l23[0]; lo8[i >> 1][4 * (i & 1) + 3] = l23[1];
+                q8[i >> 1][4 * (i & 1) + 0] = q01[0]; q8[i >> 1][4 * (i & 1) + 1] = q01[1];
+                q8[i >> 1][4 * (i & 1) + 2] = q23[0]; q8[i >> 1][4 * (i & 1) + 3] = q23[1];
             }
-            half8 *dh = reinterpret_cast<half8 *>(&T.khi[key * KP + 32 * blk + 16 * hh]);
-            half8 *dl = reinterpret_cast<half8 *>(&T.klo[key * KP + 32 * blk + 16 * hh]);
-            dh[0] = hi8[0]; dh[1] = hi8[1];
-            dl[0] = lo8[0]; dl[1] = lo8[1];
+            half8 *dk = reinterpret_cast<half8 *>(&T.k[key * KP + 16 * qq]);
+            dk[0] = q8[0];
+            dk[1] = q8[1];
+            // the key's two logit scales, computed by its 4 lanes alike (lanes qq = 0, 2 store kr
+            // and 1, 3 km, the same values twice: no branch); keys past the chunk end get 0
+            // (their raw bytes may be anything; they are masked)
+            const float d0 = (float)*reinterpret_cast<const _Float16 *>(rr);
+            const float d1 = (float)*reinterpret_cast<const _Float16 *>(rr + 34);
+            const float den = d1 != 0.f ? d1 : 1.f;
+            // d0 / den: reciprocal, product and one residual correction (within an ulp or so;
+            // no branchy IEEE division sequence in the tile loop)
+            const float rcp = __builtin_amdgcn_rcpf(den);
+            const float r0 = d0 * rcp;
+            const float kr = __builtin_fmaf(__builtin_fmaf(-den, r0, d0), rcp, r0);
+            const float sc = (qq & 1) ? den * kScaleLog2 : kr;
+            ((qq & 1) ? T.km : T.kr)[key] = key < valid_keys ? sc : 0.f;
         }
         { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
             // dims 4*dg .. 4*dg+3 sit at byte 2 + 4*dg + 2*blk of the row (block 1 skips the
@@ -222,7 +234,7 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
         { // K: straight copy into the padded tile
             const int key = tid >> 2, qq = tid & 3;
             const u32x4 *src = reinterpret_cast<const u32x4 *>(rk + key * 128 + 32 * qq);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(&T.khi[key * KP + 16 * qq]);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(&T.k[key * KP + 16 * qq]);
             dst[0] = src[0];
             dst[1] = src[1];
         }
@@ -322,7 +334,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 
     half8 qreg[NJ][4];
     floatx16 o[NJ][2];
-    float l_part[NJ], m_raw[NJ], m_ref[NJ];
+    float l_part[NJ], m_top[NJ], m_ref[NJ];
     bool saw[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             o[j][1][v] = 0.f;
         }
         l_part[j] = 0.f;
-        m_raw[j] = -INFINITY; // running max of the raw dot products Q.K (= scaled logit * 8)
+        m_top[j] = -INFINITY; // running maximum of the logits, log2 units
         m_ref[j] = -INFINITY; // reference maximum of the exponentials, log2 units
         saw[j] = false;
         if (kv_end_b[j] > 0 && q_ok[j]) {
@@ -345,8 +357,8 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             // wavefront only; the other starts empty and is merged in at the end)
             const float mo = (!SPLIT || kh == 0) ? a.m[row[j]] : -INFINITY;
             if (mo != -INFINITY) {
-                m_raw[j] = mo * 8.0f;
-                m_ref[j] = m_raw[j] * kScaleLog2;
+                m_top[j] = mo * kLog2e;
+                m_ref[j] = m_top[j];
                 if (g == 0)
                     l_part[j] = a.l[row[j]];
                 const float4 *orow = reinterpret_cast<const float4 *>(a.o + row[j] * kHeadDim);
@@ -433,7 +445,8 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         if (key0 < kv_end_w) {
             // S^T = K Q^T: lane (qcol, g) holds
             // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][si][v], sub the
-            // si-th key subtile this wavefront covers
+            // si-th key subtile this wavefront covers.  Q8_0: the first block's products (dims
+            // 0-31) are scaled by kr before the second block's are added.
             floatx16 s[NJ][NS];
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
@@ -443,28 +456,61 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     for (int v = 0; v < 16; ++v)
                         s[j][si][v] = 0.f;
 #pragma unroll
-            for (int si = 0; si < NS; ++si) {
-                const int sub = SPLIT ? kh : si;
-                const int kr = (32 * sub + qcol) * KP + 8 * g;
+            for (int half = 0; half < 2; ++half)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const half8 ah = *reinterpret_cast<const half8 *>(&T.khi[kr + 16 * kk]);
+                for (int si = 0; si < NS; ++si) {
+                    const int sub = SPLIT ? kh : si;
+                    const int krow = (32 * sub + qcol) * KP + 8 * g;
+                    if (FMT == 0 && half == 1) {
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qreg[j][kk],
-                                                                         s[j][si], 0, 0, 0);
-                    if constexpr (FMT == 0) {
-                        const half8 al = *reinterpret_cast<const half8 *>(&T.klo[kr + 16 * kk]);
+                        for (int i = 0; i < 4; ++i) {
+                            const float4 r4 =
+                                *reinterpret_cast<const float4 *>(&T.kr[32 * sub + 8 * i + 4 * g]);
+#pragma unroll
+                            for (int j = 0; j < NJ; ++j) {
+                                s[j][si][4 * i + 0] *= r4.x;
+                                s[j][si][4 * i + 1] *= r4.y;
+                                s[j][si][4 * i + 2] *= r4.z;
+                                s[j][si][4 * i + 3] *= r4.w;
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int kk = 2 * half; kk < 2 * half + 2; ++kk) {
+                        const half8 ak = *reinterpret_cast<const half8 *>(&T.k[krow + 16 * kk]);
 #pragma unroll
                         for (int j = 0; j < NJ; ++j)
-                            s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                al, qreg[j][kk], s[j][si], 0, 0, 0);
+                            s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[j][kk],
+                                                                             s[j][si], 0, 0, 0);
                     }
                 }
-            }
             // independent VALU work for the matrix instructions above to overlap with
             unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
+
+            // u = S*log2(e)/8 - ref, the exponent relative to the reference maximum before
+            // this tile (0 while it is -inf)
+            float base[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                base[j] = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
+#pragma unroll
+            for (int si = 0; si < NS; ++si) {
+                const int sub = SPLIT ? kh : si;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float4 m4 = {kScaleLog2, kScaleLog2, kScaleLog2, kScaleLog2};
+                    if constexpr (FMT == 0)
+                        m4 = *reinterpret_cast<const float4 *>(&T.km[32 * sub + 8 * i + 4 * g]);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        s[j][si][4 * i + 0] = __builtin_fmaf(s[j][si][4 * i + 0], m4.x, -base[j]);
+                        s[j][si][4 * i + 1] = __builtin_fmaf(s[j][si][4 * i + 1], m4.y, -base[j]);
+                        s[j][si][4 * i + 2] = __builtin_fmaf(s[j][si][4 * i + 2], m4.z, -base[j]);
+                        s[j][si][4 * i + 3] = __builtin_fmaf(s[j][si][4 * i + 3], m4.w, -base[j]);
+                    }
+                }
+            }
 
             // The 32-key subtiles that some row of a block cannot wholly see (causal diagonal,
             // ragged chunk end, padding rows) are masked element by element; the common case
@@ -487,10 +533,10 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                 }
             }
             bool need_any = false;
-            float mx2[NJ];
+            float mx[NJ];
+            bool need[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                float mx;
                 if constexpr (NS == 2) {
                     float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
                     float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
@@ -499,45 +545,49 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                         ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
                         mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
                     }
-                    mx = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
+                    mx[j] = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
                 } else {
                     float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
 #pragma unroll
                     for (int v = 3; v < 15; v += 2)
                         ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
-                    mx = fmaxf(ma, s[j][0][15]);
+                    mx[j] = fmaxf(ma, s[j][0][15]);
                 }
-                mx = half_swap_max(mx);
-                m_raw[j] = fmaxf(m_raw[j], mx);
-                saw[j] = saw[j] || (mx != -INFINITY);
-                mx2[j] = mx * kScaleLog2;
-                need_any = need_any || (mx2[j] > m_ref[j] + kTau);
+                mx[j] = half_swap_max(mx[j]); // tile maximum of u for this query row
+                m_top[j] = fmaxf(m_top[j], base[j] + mx[j]);
+                saw[j] = saw[j] || (mx[j] != -INFINITY);
+                // raise the reference when the tile's maximum exceeds it by more than kTau (or
+                // when it is still -inf and the row saw a key)
+                need[j] = mx[j] > (m_ref[j] == -INFINITY ? -INFINITY : kTau);
+                need_any = need_any || need[j];
             }
             if (__builtin_amdgcn_ballot_w64(need_any)) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const float m_new = mx2[j] > m_ref[j] + kTau ? mx2[j] : m_ref[j];
+                    const float delta = need[j] ? mx[j] : 0.f; // new ref = base + delta
                     const float alpha = (m_ref[j] == -INFINITY)
-                                            ? 0.f : __builtin_amdgcn_exp2f(m_ref[j] - m_new);
+                                            ? 0.f : __builtin_amdgcn_exp2f(-delta);
                     l_part[j] *= alpha;
                     o[j][0] *= alpha;
                     o[j][1] *= alpha;
-                    m_ref[j] = m_new;
+                    if (need[j])
+                        m_ref[j] = base[j] + delta;
+#pragma unroll
+                    for (int si = 0; si < NS; ++si)
+                        s[j][si] -= delta;
                 }
             }
-            // per query block: P = exp2(S*log2e/8 - ref) (l sums the FP32 values), P to FP16,
-            // then O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
+            // per query block: P = exp2(u) (l sums the FP32 values), P to FP16, then
+            // O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const float base = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
                 float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
                 half8 p16[NS][2];
 #pragma unroll
                 for (int si = 0; si < NS; ++si) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const float p = __builtin_amdgcn_exp2f(
-                            __builtin_fmaf(s[j][si][v], kScaleLog2, -base));
+                        const float p = __builtin_amdgcn_exp2f(s[j][si][v]);
                         s[j][si][v] = p;
                         ls[v & 3] += p;
                     }
@@ -583,7 +633,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             }
             xb[32] = l_part[0];
             xb[33] = m_ref[0];
-            xb[34] = m_raw[0];
+            xb[34] = m_top[0];
             xb[35] = saw[0] ? 1.f : 0.f;
         }
         __syncthreads();
@@ -602,7 +652,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                 l_part[0] = l_part[0] * fa + xb[32] * fb;
                 m_ref[0] = mn;
             }
-            m_raw[0] = fmaxf(m_raw[0], xb[34]);
+            m_top[0] = fmaxf(m_top[0], xb[34]);
             saw[0] = saw[0] || xb[35] != 0.f;
         }
     }
@@ -613,7 +663,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         if (kv_end_b[j] > 0 && (!SPLIT || kh == 0)) { // uniform per wavefront
             const float l_tot = half_swap_sum(l_part[j]);
             if (q_ok[j] && saw[j]) {
-                const float rr = __builtin_amdgcn_exp2f(m_ref[j] - m_raw[j] * kScaleLog2);
+                const float rr = __builtin_amdgcn_exp2f(m_ref[j] - m_top[j]);
                 float4 *orow = reinterpret_cast<float4 *>(a.o + row[j] * kHeadDim);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -624,7 +674,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                                     o[j][1][4 * k + 2] * rr, o[j][1][4 * k + 3] * rr);
                 }
                 if (g == 0) {
-                    a.m[row[j]] = m_raw[j] * 0.125f;
+                    a.m[row[j]] = m_top[j] * kLn2;
                     a.l[row[j]] = l_tot * rr;
                 }
             }
