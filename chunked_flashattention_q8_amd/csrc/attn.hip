@@ -68,6 +68,19 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes per lane from a buffer resource straight into LDS: lane l's bytes land at
+// lds_base + 16 * l (lds_base wavefront-uniform).  Written as inline assembly so that the
+// compiler's automatic waits do not treat every later LDS read as possibly aliasing the copy
+// (it cannot tell the copies' destination from the operand tiles, and would wait for each copy
+// right after issuing it); the kernel waits for the copies explicitly before its barriers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // Signed bytes -> FP16 values (exact).  Each byte is biased to unsigned (x ^ 0x80) and placed as
 // the low mantissa byte of 1024.0 (0x64 high byte), giving 1024 + 128 + x; subtracting 1152
 // leaves x.  v_perm_b32 picks bytes from {S0, S1} (selector 0-3: S1's bytes, 4-7: S0's), so
@@ -332,53 +345,6 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         kv_full_w = min(kv_full_w, kv_full_b[j]);
     }
 
-    half8 qreg[NJ][4];
-    floatx16 o[NJ][2];
-    float l_part[NJ], m_top[NJ], m_ref[NJ];
-    bool saw[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            o[j][0][v] = 0.f;
-            o[j][1][v] = 0.f;
-        }
-        l_part[j] = 0.f;
-        m_top[j] = -INFINITY; // running maximum of the logits, log2 units
-        m_ref[j] = -INFINITY; // reference maximum of the exponentials, log2 units
-        saw[j] = false;
-        if (kv_end_b[j] > 0 && q_ok[j]) {
-            const half8 *qrow = reinterpret_cast<const half8 *>(
-                reinterpret_cast<const _Float16 *>(a.q) + row[j] * kHeadDim);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qreg[j][kk] = qrow[2 * kk + g];
-            // non-empty row: resume from its state (SPLIT: in the first key subtile's
-            // wavefront only; the other starts empty and is merged in at the end)
-            const float mo = (!SPLIT || kh == 0) ? a.m[row[j]] : -INFINITY;
-            if (mo != -INFINITY) {
-                m_top[j] = mo * kLog2e;
-                m_ref[j] = m_top[j];
-                if (g == 0)
-                    l_part[j] = a.l[row[j]];
-                const float4 *orow = reinterpret_cast<const float4 *>(a.o + row[j] * kHeadDim);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float4 x = orow[2 * k + g];
-                    const float4 y = orow[8 + 2 * k + g];
-                    o[j][0][4 * k + 0] = x.x; o[j][0][4 * k + 1] = x.y;
-                    o[j][0][4 * k + 2] = x.z; o[j][0][4 * k + 3] = x.w;
-                    o[j][1][4 * k + 0] = y.x; o[j][1][4 * k + 1] = y.y;
-                    o[j][1][4 * k + 2] = y.z; o[j][1][4 * k + 3] = y.w;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qreg[j][kk] = half8{};
-        }
-    }
-
     // ---- K/V tile pipeline: raw rows of tile t+2 are fetched into registers while tile t is
     // computed and tile t+1 is unpacked; one barrier per tile.
     const uint8_t *kbase = a.k + b * a.kv_seq_stride + h * a.kv_head_stride;
@@ -420,8 +386,9 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             if (slot(sl, tensor, piece)) {
                 const uint32_t off = (uint32_t)t * (KT * ROW) + 16u * piece;
                 uint8_t *dst = &sm.raw[buf][tensor][16 * (piece - lane)];
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(tensor ? rv : rk, (lds_void *)dst, 16, off,
-                                                         0, 0, 0);
+                const uint32_t base = __builtin_amdgcn_readfirstlane(
+                    (uint32_t)(uintptr_t)(lds_void *)dst);
+                dma16(tensor ? rv : rk, off, base);
             }
         }
     };
@@ -429,14 +396,81 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     // Loads past the chunk read as zero, and operand tiles unpacked from raw rows past the last
     // tile are never read, so fetch and unpack run unconditionally (no branches inside the
     // tile loop's scheduling regions).
+    // Prologue: the first two tiles' copies, then every row's Q and m, all in flight together;
+    // the resumed rows' l and O are loaded after it, their latency covered by the first tile's
+    // QK work (they are first used by its rescale or PV products).
     fetch(0, 0);
     fetch(1, 1);
+
+    half8 qreg[NJ][4];
+    floatx16 o[NJ][2];
+    float l_part[NJ], m_top[NJ], m_ref[NJ], m_old[NJ];
+    bool saw[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            o[j][0][v] = 0.f;
+            o[j][1][v] = 0.f;
+        }
+        l_part[j] = 0.f;
+        m_top[j] = -INFINITY; // running maximum of the logits, log2 units
+        m_ref[j] = -INFINITY; // reference maximum of the exponentials, log2 units
+        saw[j] = false;
+        m_old[j] = -INFINITY;
+        if (kv_end_b[j] > 0 && q_ok[j]) {
+            const half8 *qrow = reinterpret_cast<const half8 *>(
+                reinterpret_cast<const _Float16 *>(a.q) + row[j] * kHeadDim);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qreg[j][kk] = qrow[2 * kk + g];
+            // SPLIT: only the first key subtile's wavefront resumes from the state; the other
+            // starts empty and is merged in at the end
+            if (!SPLIT || kh == 0)
+                m_old[j] = a.m[row[j]];
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qreg[j][kk] = half8{};
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0); // the copies have landed in LDS before the barrier
     __syncthreads();
     unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        if (m_old[j] != -INFINITY) {
+            m_top[j] = m_old[j] * kLog2e;
+            m_ref[j] = m_top[j];
+        }
+    // l and O of the resumed rows, this head's rows of the state as buffers: lanes of rows
+    // that are empty (or whose l another lane reads) address past the range and read 0,
+    // so the loads need no branch
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(a.o + head * a.M * kHeadDim,
+                                                  (uint32_t)a.M * kHeadDim * 4u);
+    const __amdgpu_buffer_rsrc_t rs_l = make_rsrc(a.l + head * a.M, (uint32_t)a.M * 4u);
+    auto load_resumed = [&]() {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const bool res = m_old[j] != -INFINITY;
+            const uint32_t ob = res ? (uint32_t)qi[j] * (kHeadDim * 4u) : 0x80000000u;
+            const uint32_t lb = (res && g == 0) ? (uint32_t)qi[j] * 4u : 0x80000000u;
+            l_part[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_l, lb, 0, 0));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u32x4 x = load16(rs_o, ob + 16u * (2 * k + g));
+                const u32x4 y = load16(rs_o, ob + 16u * (8 + 2 * k + g));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[j][0][4 * k + e] = __uint_as_float(x[e]);
+                    o[j][1][4 * k + e] = __uint_as_float(y[e]);
+                }
+            }
+        }
+    };
 
-    for (int t = 0; t < n_tiles; ++t) {
+    auto tile = [&](const int t) {
         fetch(t + 2, t & 1); // raw buffer t&1 was unpacked in the previous interval
         const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
@@ -617,7 +651,13 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         }
         __builtin_amdgcn_s_waitcnt(0); // raw rows of tile t+2 have landed before the barrier
         __syncthreads();
-    }
+    };
+    // The first tile is peeled: the state loads are issued right before its copies, so the
+    // wait in front of their first use leaves those copies in flight.
+    load_resumed();
+    tile(0);
+    for (int t = 1; t < n_tiles; ++t)
+        tile(t);
 
     if constexpr (SPLIT) {
         // merge the two key subtiles' states of each block: the second subtile's wavefront
