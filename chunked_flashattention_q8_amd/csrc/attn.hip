@@ -345,8 +345,8 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         kv_full_w = min(kv_full_w, kv_full_b[j]);
     }
 
-    // ---- K/V tile pipeline: raw rows of tile t+2 are fetched into registers while tile t is
-    // computed and tile t+1 is unpacked; one barrier per tile.
+    // ---- K/V tile pipeline: raw rows of tile t+2 are copied into LDS while tile t is computed
+    // and tile t+1 is unpacked; one barrier per tile.
     const uint8_t *kbase = a.k + b * a.kv_seq_stride + h * a.kv_head_stride;
     const uint8_t *vbase = a.v + b * a.kv_seq_stride + h * a.kv_head_stride;
     // The range is rounded up to 16 bytes: the last 16-byte piece may hold up to 12 bytes past
@@ -697,26 +697,45 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         }
     }
 
-    // ---- write back the rows that saw at least one key, renormalised to the true maximum
+    // ---- write back the rows that saw at least one key, renormalised to the true maximum.
+    // Each wavefront stages its 32-row block in LDS (its own region, past the area the merge
+    // above uses) and stores whole rows: 4 contiguous rows (1 KiB) per store instruction, instead
+    // of 32-byte pieces of 32 rows.  A row's write flag travels with it.
+    constexpr int kStagePitch = 68;                                // floats per staged row
+    constexpr int kStageFloats = WQ * kStagePitch + WQ;            // rows, then the flags
+    constexpr int kStageBase = 2 * 64 * 36;                        // floats
+    static_assert(sizeof(Smem<FMT>) >= 4 * (kStageBase + 4 * kStageFloats), "staging area");
+    float *stg = reinterpret_cast<float *>(&sm) + kStageBase + wave * kStageFloats;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (kv_end_b[j] > 0 && (!SPLIT || kh == 0)) { // uniform per wavefront
             const float l_tot = half_swap_sum(l_part[j]);
-            if (q_ok[j] && saw[j]) {
-                const float rr = __builtin_amdgcn_exp2f(m_ref[j] - m_top[j]);
-                float4 *orow = reinterpret_cast<float4 *>(a.o + row[j] * kHeadDim);
+            const bool wr = q_ok[j] && saw[j];
+            const float rr = wr ? __builtin_amdgcn_exp2f(m_ref[j] - m_top[j]) : 0.f;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    orow[2 * k + g] = make_float4(o[j][0][4 * k] * rr, o[j][0][4 * k + 1] * rr,
-                                                  o[j][0][4 * k + 2] * rr, o[j][0][4 * k + 3] * rr);
-                    orow[8 + 2 * k + g] =
-                        make_float4(o[j][1][4 * k] * rr, o[j][1][4 * k + 1] * rr,
-                                    o[j][1][4 * k + 2] * rr, o[j][1][4 * k + 3] * rr);
-                }
-                if (g == 0) {
+            for (int k = 0; k < 4; ++k) {
+                *reinterpret_cast<float4 *>(&stg[qcol * kStagePitch + 8 * k + 4 * g]) =
+                    make_float4(o[j][0][4 * k] * rr, o[j][0][4 * k + 1] * rr,
+                                o[j][0][4 * k + 2] * rr, o[j][0][4 * k + 3] * rr);
+                *reinterpret_cast<float4 *>(&stg[qcol * kStagePitch + 32 + 8 * k + 4 * g]) =
+                    make_float4(o[j][1][4 * k] * rr, o[j][1][4 * k + 1] * rr,
+                                o[j][1][4 * k + 2] * rr, o[j][1][4 * k + 3] * rr);
+            }
+            if (g == 0) {
+                stg[WQ * kStagePitch + qcol] = wr ? 1.f : 0.f;
+                if (wr) {
                     a.m[row[j]] = m_top[j] * kLn2;
                     a.l[row[j]] = l_tot * rr;
                 }
+            }
+            // the same wavefront reads back what it wrote (LDS keeps a wavefront's order)
+            float4 *oblk = reinterpret_cast<float4 *>(a.o + (row[j] - qcol) * kHeadDim);
+#pragma unroll
+            for (int i = 0; i < WQ / 4; ++i) {
+                const int r = 4 * i + (lane >> 4), c = lane & 15;
+                const float4 v = *reinterpret_cast<const float4 *>(&stg[r * kStagePitch + 4 * c]);
+                if (stg[WQ * kStagePitch + r] != 0.f)
+                    oblk[r * (kHeadDim / 4) + c] = v;
             }
         }
     }
