@@ -54,3 +54,21 @@ def test_pack_workload_kv(orc, wid):
         got = gpu_pack(x)
         torch.cuda.synchronize()
         assert np.array_equal(got.cpu().numpy(), orc.q8_0_pack(x)), name
+
+
+@pytest.mark.parametrize("n_rows,row_len,offset", [(3, 32, 2), (1001, 32, 2), (777, 96, 2),
+                                                   (777, 96, 4), (130, 32, 0)])
+def test_pack_destination_alignment_and_odd_block_counts(orc, n_rows, row_len, offset):
+    """dst only 2-byte aligned (offset 2) and odd block counts (the last 2-byte piece of a
+    workgroup's range); the bytes around the packed range are left untouched."""
+    rng = np.random.default_rng(n_rows + offset)
+    x = rng.standard_normal((n_rows, row_len)).astype(np.float32)
+    xt = torch.from_numpy(x).to(dev())
+    n_bytes = n_rows * row_len // 32 * 34
+    buf = torch.full((n_bytes + 16,), 0xA5, dtype=torch.uint8, device=dev())
+    say("pack to offset", offset, n_rows, row_len)
+    q8a.q8_0_pack(xt, buf.data_ptr() + offset, n_rows, row_len)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[offset:offset + n_bytes], orc.q8_0_pack(x).reshape(-1))
+    assert (got[:offset] == 0xA5).all() and (got[offset + n_bytes:] == 0xA5).all()
