@@ -34,7 +34,8 @@ STATE_MAGIC = 0x51384154
 HEAD_DIM = 64
 ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
 
-EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_finalize",
+EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_append_chunk",
+           "attn_finalize",
            "attn_state_merge", "attn_accumulate_stream", "q8a_status_string",
            "q8a_last_hip_error")
 
@@ -75,6 +76,7 @@ def library() -> ctypes.CDLL:
     lib.q8_0_pack.argtypes = [P, P, i64, i32, P]
     lib.attn_state_init.argtypes = [SP, P, P, P, i32, i32, i32, i32, i64, P]
     lib.attn_accumulate_chunk.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P]
+    lib.attn_append_chunk.argtypes = [SP, P, P, P, P, P, i64, i32, i64, i64, i32, P]
     lib.attn_finalize.argtypes = [SP, P, P, P]
     lib.attn_state_merge.argtypes = [SP, SP, P]
     lib.attn_accumulate_stream.argtypes = [SP, P, P, P, i32, i64, i32, ctypes.POINTER(P),
@@ -83,8 +85,8 @@ def library() -> ctypes.CDLL:
     lib.q8a_status_string.argtypes = [ctypes.c_int]
     lib.q8a_last_hip_error.restype = ctypes.c_int
     lib.q8a_last_hip_error.argtypes = []
-    for name in ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_finalize",
-                 "attn_state_merge", "attn_accumulate_stream"):
+    for name in ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_append_chunk",
+                 "attn_finalize", "attn_state_merge", "attn_accumulate_stream"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -138,6 +140,17 @@ def attn_accumulate_chunk(st: q8a_state, q, k, v, kv_dtype: int, kv_pos0: int, n
                                            int(kv_dtype), int(kv_pos0), int(n_kv),
                                            int(kv_head_stride), int(kv_seq_stride),
                                            int(causal), _stream(stream)))
+
+
+def attn_append_chunk(st: q8a_state, q, k_new, v_new, k_cache, v_cache, kv_pos0: int, n_kv: int,
+                      kv_head_stride: int, kv_seq_stride: int, causal: int = 1,
+                      stream=None) -> None:
+    """Pack n_kv new FP32 K/V tokens into the Q8_0 cache rows at k_cache / v_cache and fold
+    them into the state (the same bytes and state as q8_0_pack + attn_accumulate_chunk)."""
+    _check(library().attn_append_chunk(ctypes.byref(st), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       _ptr(k_cache), _ptr(v_cache), int(kv_pos0), int(n_kv),
+                                       int(kv_head_stride), int(kv_seq_stride), int(causal),
+                                       _stream(stream)))
 
 
 def attn_finalize(st: q8a_state, out, lse=None, stream=None) -> None:

@@ -174,6 +174,56 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
+int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
+                      const float *v_new, void *k_cache, void *v_cache, int64_t kv_pos0,
+                      int32_t n_kv, int64_t kv_head_stride, int64_t kv_seq_stride,
+                      int32_t causal, void *stream)
+{
+    int rc = check_chunk(st, q, k_cache, v_cache, Q8A_KV_Q8_0, kv_pos0, n_kv, kv_head_stride,
+                         kv_seq_stride, causal);
+    if (rc)
+        return rc;
+    if (!k_new || !v_new)
+        return Q8A_E_INVAL;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16))
+        return Q8A_E_ALIGN;
+    const int64_t runs = (int64_t)st->n_seq * st->n_heads;
+    if (runs > 65535)
+        return Q8A_E_UNSUPPORTED;
+    if (kv_head_stride > ((int64_t)1 << 46) || kv_seq_stride > ((int64_t)1 << 46))
+        return Q8A_E_INVAL; // keeps the span products below in range
+    const int64_t row_span = (int64_t)n_kv * q8a::kQ8RowBytes;
+    // every (sequence, head) destination run must be its own: sequences outside heads or heads
+    // outside sequences (check_chunk covers the single-sequence and single-head cases)
+    if (st->n_seq > 1 && st->n_heads > 1 &&
+        !(kv_seq_stride >= (st->n_heads - 1) * kv_head_stride + row_span ||
+          kv_head_stride >= (st->n_seq - 1) * kv_seq_stride + row_span))
+        return Q8A_E_INVAL;
+    // K and V destinations must not overlap each other or the sources
+    const int64_t dst_span = (int64_t)(st->n_seq - 1) * kv_seq_stride +
+                             (int64_t)(st->n_heads - 1) * kv_head_stride + row_span;
+    const int64_t src_span = runs * n_kv * q8a::kHeadDim * 4;
+    auto overlap = [](const void *a, int64_t na, const void *b, int64_t nb) {
+        const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+        return x < y + nb && y < x + na;
+    };
+    if (overlap(k_cache, dst_span, v_cache, dst_span) ||
+        overlap(k_cache, dst_span, k_new, src_span) || overlap(k_cache, dst_span, v_new, src_span) ||
+        overlap(v_cache, dst_span, k_new, src_span) || overlap(v_cache, dst_span, v_new, src_span))
+        return Q8A_E_INVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = q8a::launch_q8_0_pack_rows(k_new, v_new, static_cast<uint8_t *>(k_cache),
+                                              static_cast<uint8_t *>(v_cache), st->n_seq,
+                                              st->n_heads, n_kv, kv_head_stride, kv_seq_stride,
+                                              s);
+    if (e != hipSuccess)
+        return hip_failure(e);
+    q8a::AccumulateArgs a = make_args(st, q, k_cache, v_cache, kv_pos0, n_kv, kv_head_stride,
+                                      kv_seq_stride, causal);
+    e = q8a::launch_accumulate(a, Q8A_KV_Q8_0, s);
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
 int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream)
 {
     int rc = check_state(st);

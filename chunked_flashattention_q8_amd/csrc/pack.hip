@@ -29,12 +29,26 @@ __device__ __forceinline__ int quantise(float x, float dh)
 }
 
 // Each lane packs its quarter of U blocks (U x 256 consecutive float4 per workgroup); the U loads
-// are issued before any is used.
+// are issued before any is used.  blockIdx.y selects a run of n_blocks blocks (one (sequence,
+// head) pair of an appended chunk: its source at x + y * n_blocks * 8 float4, its destination
+// at dst + (y / n_heads) * seq_stride + (y % n_heads) * head_stride) and blockIdx.z the tensor
+// (K from x / dst, V from x2 / dst2); a flat pack is the single run y = z = 0.
 template <int U>
 __global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict__ x,
                                                          uint8_t *__restrict__ dst,
-                                                         int64_t n_blocks)
+                                                         int64_t n_blocks,
+                                                         const float4 *__restrict__ x2,
+                                                         uint8_t *__restrict__ dst2,
+                                                         int32_t n_heads, int64_t head_stride,
+                                                         int64_t seq_stride)
 {
+    const int run = blockIdx.y;
+    if (blockIdx.z) {
+        x = x2;
+        dst = dst2;
+    }
+    x += (int64_t)run * n_blocks * 8;
+    dst += (int64_t)(run / n_heads) * seq_stride + (int64_t)(run % n_heads) * head_stride;
     float4 v[U];
     int64_t blk[U];
 #pragma unroll
@@ -68,15 +82,31 @@ __global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict
 
 } // namespace
 
+constexpr int kPackU = 2; // blocks per lane group of 8 (two 16-byte loads in flight per lane)
+
 hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s)
 {
     if (n_blocks == 0)
         return hipSuccess;
-    constexpr int U = 2; // blocks per lane group of 8 (two 16-byte loads in flight per lane)
     const int64_t threads = n_blocks * 8;
-    const int64_t grid = (threads + 256 * U - 1) / (256 * U);
-    hipLaunchKernelGGL(q8_0_pack_kernel<U>, dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const float4 *>(x), dst, n_blocks);
+    const int64_t grid = (threads + 256 * kPackU - 1) / (256 * kPackU);
+    hipLaunchKernelGGL(q8_0_pack_kernel<kPackU>, dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(x), dst, n_blocks,
+                       reinterpret_cast<const float4 *>(x), dst, 1, (int64_t)0, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_0_pack_rows(const float *k, const float *v, uint8_t *k_dst, uint8_t *v_dst,
+                                 int32_t n_seq, int32_t n_heads, int32_t n_rows,
+                                 int64_t head_stride, int64_t seq_stride, hipStream_t s)
+{
+    const int64_t n_blocks = (int64_t)n_rows * (kHeadDim / 32); // per (sequence, head) run
+    const int64_t grid = (n_blocks * 8 + 256 * kPackU - 1) / (256 * kPackU);
+    hipLaunchKernelGGL(q8_0_pack_kernel<kPackU>,
+                       dim3((unsigned)grid, (unsigned)(n_seq * n_heads), 2), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(k), k_dst, n_blocks,
+                       reinterpret_cast<const float4 *>(v), v_dst, n_heads, head_stride,
+                       seq_stride);
     return hipGetLastError();
 }
 

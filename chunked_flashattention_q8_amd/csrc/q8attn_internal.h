@@ -27,6 +27,11 @@ struct AccumulateArgs {
 };
 
 hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s);
+// K and V rows [n_seq][n_heads][n_rows][64] FP32 -> Q8_0 rows at k_dst / v_dst + b * seq_stride
+// + h * head_stride + j * 68 (one launch for both tensors)
+hipError_t launch_q8_0_pack_rows(const float *k, const float *v, uint8_t *k_dst, uint8_t *v_dst,
+                                 int32_t n_seq, int32_t n_heads, int32_t n_rows,
+                                 int64_t head_stride, int64_t seq_stride, hipStream_t s);
 hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s);
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s);
 hipError_t launch_finalize(const float *m, const float *l, const float *o, void *out,

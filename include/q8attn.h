@@ -109,6 +109,27 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
                           int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
                           void *stream);
 
+/* Quantise-on-append: pack n_kv newly appended tokens of K and V into the Q8_0 cache and
+ * accumulate them into the state, in one call.  The cache entries are quantised dynamically as
+ * they arrive ("Core Architecture & The 4-Brick Pipeline", Sec. 5: dynamically quantised
+ * block_q8_0 KV; the append of Mode A in "Out-of-Core ...", Sec. 4).  The result is exactly that of
+ * q8_0_pack of each new row into its cache row followed by attn_accumulate_chunk over those rows:
+ * the same cache bytes, the same state bits.
+ *   k_new, v_new   FP32 [n_seq][n_heads][n_kv][64], C-contiguous, 16-byte aligned (device).
+ *   k_cache, v_cache  destination of new key 0 for sequence 0, head 0; key j of (seq b, head h)
+ *            goes to  k_cache + b*kv_seq_stride + h*kv_head_stride + j*68.  Same alignment, stride
+ *            and over-read rules as attn_accumulate_chunk with kv_dtype Q8_0; strides at most
+ *            2^46 bytes.  With several sequences and several heads, the (sequence, head) runs must
+ *            not interleave: kv_seq_stride >= (n_heads-1)*kv_head_stride + n_kv*68, or the same
+ *            with the roles swapped.  The K and V destinations must not overlap each other or
+ *            the FP32 sources (Q8A_E_INVAL).  Only the n_kv*68 bytes of each run are written.
+ *   q, kv_pos0, n_kv, causal, stream: as for attn_accumulate_chunk.
+ * Two launches on the stream (one pack of both tensors, one accumulate). */
+int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
+                      const float *v_new, void *k_cache, void *v_cache, int64_t kv_pos0,
+                      int32_t n_kv, int64_t kv_head_stride, int64_t kv_seq_stride,
+                      int32_t causal, void *stream);
+
 /* Final output after the last chunk ("Out-of-Core ...", Sec. 3): out = O / l rounded once to
  * FP16 (nearest even), and lse = m + ln(l) in FP32 (natural log).  Empty rows give out = 0 and
  * lse = -inf.  out: FP16 [n_seq][n_heads][n_q][64], 16-byte aligned; lse: FP32 [..][n_q] or NULL.

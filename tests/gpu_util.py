@@ -41,10 +41,10 @@ def gpu_pack(x: np.ndarray) -> torch.Tensor:
 
 
 def prefill(q, k, v, kv_dtype, B, H, M, N, q_pos0, chunks, causal=1, on_state=None,
-            state=None):
+            state=None, finalize=True):
     """init -> one attn_accumulate_chunk per (kv_pos0, n_kv) -> finalize, on the current stream.
     k, v: device tensors [B, H, N, row] (bytes) or [B, H, N, 64] FP16.  Returns (out, lse,
-    (m, l, o)) as device tensors."""
+    (m, l, o)) as device tensors (out and lse None without the finalize)."""
     row = q8a.ROW_BYTES[kv_dtype]
     if state is None:
         m, l, o = q8a.alloc_state(B, H, M)
@@ -58,6 +58,8 @@ def prefill(q, k, v, kv_dtype, B, H, M, N, q_pos0, chunks, causal=1, on_state=No
         if on_state is not None:
             torch.cuda.synchronize()
             on_state(s, n, m, l, o)
+    if not finalize:
+        return None, None, (m, l, o)
     out = torch.empty((B, H, M, D), dtype=torch.float16, device=dev())
     lse = torch.empty((B, H, M), dtype=torch.float32, device=dev())
     q8a.attn_finalize(st, out, lse)

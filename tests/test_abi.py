@@ -118,6 +118,50 @@ def test_accumulate_rejects_bad_arguments():
     assert acc(st2, ss=0) == q8a.Q8A_E_INVAL                # sequences would overlap
 
 
+K_NEW, V_NEW, K_CACHE, V_CACHE = 0x1000000, 0x2000000, 0x3000000, 0x4000000
+
+
+def append(st, q=A16, kn=K_NEW, vn=V_NEW, kc=K_CACHE, vc=V_CACHE, pos=0, n=64, hs=None, ss=0,
+           causal=1):
+    if hs is None:
+        hs = 256 * 68
+    P = ctypes.c_void_p
+    return q8a.library().attn_append_chunk(ctypes.byref(st), P(q), P(kn), P(vn), P(kc), P(vc),
+                                           pos, n, hs, ss, causal, None)
+
+
+def test_append_rejects_bad_arguments():
+    st = fake_state()
+    assert append(q8a.q8a_state()) == q8a.Q8A_E_STATE        # not initialised
+    assert append(st, kn=0) == q8a.Q8A_E_INVAL
+    assert append(st, vn=0) == q8a.Q8A_E_INVAL
+    assert append(st, kc=0) == q8a.Q8A_E_INVAL
+    assert append(st, n=0) == q8a.Q8A_E_INVAL
+    assert append(st, causal=3) == q8a.Q8A_E_INVAL
+    assert append(st, kn=K_NEW + 4) == q8a.Q8A_E_ALIGN
+    assert append(st, vc=V_CACHE + 4) == q8a.Q8A_E_ALIGN
+    assert append(st, hs=64 * 68 - 16) == q8a.Q8A_E_INVAL     # heads' runs would overlap
+    assert append(st, hs=1 << 47) == q8a.Q8A_E_INVAL          # stride out of range
+    assert append(st, vc=K_CACHE + 4096) == q8a.Q8A_E_INVAL   # K and V destinations overlap
+    assert append(st, kc=K_NEW + 1024) == q8a.Q8A_E_INVAL     # destination over a source
+    assert append(st, vc=V_NEW) == q8a.Q8A_E_INVAL
+    st2 = fake_state(B=2)
+    # sequence stride inside the head runs: (seq 1, head 0) would land on (seq 0, head 1)
+    assert append(st2, hs=64 * 68, ss=64 * 68) == q8a.Q8A_E_INVAL
+    assert append(st2, hs=64 * 68, ss=0) == q8a.Q8A_E_INVAL
+    big = fake_state(B=300, H=300)
+    assert append(big, hs=64 * 68, ss=300 * 64 * 68) == q8a.Q8A_E_UNSUPPORTED
+
+
+@pytest.mark.skipif(not NO_GPU, reason="needs a host without a GPU")
+def test_append_valid_layouts_pass_validation():
+    """Heads outside sequences and sequences outside heads are both accepted (validation passes
+    and the launch then fails for want of a device)."""
+    st2 = fake_state(B=2)
+    assert append(st2, hs=64 * 68, ss=4 * 64 * 68) == q8a.Q8A_E_HIP
+    assert append(st2, hs=2 * 64 * 68, ss=64 * 68) == q8a.Q8A_E_HIP
+
+
 def test_finalize_rejects_bad_arguments():
     lib = q8a.library()
     P = ctypes.c_void_p

@@ -10,7 +10,8 @@ import torch
 
 import chunked_flashattention_q8_amd as q8a
 import synthetic
-from gpu_util import (D, assert_close, f16_to_dev, gpu_pack, metrics, prefill, rows_of, say)
+from gpu_util import (D, assert_close, dev, f16_to_dev, gpu_pack, metrics, prefill, rows_of,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -172,7 +173,7 @@ def test_empty_state_finalize():
 
 # ---------------------------------------------------------------- the workloads' own shapes
 
-def run_workload(orc, wid, kv_dtype=q8a.KV_Q8_0, chunk=None, rows_per_head=None):
+def run_workload(orc, wid, kv_dtype=q8a.KV_Q8_0, chunk=None, rows_per_head=None, append=False):
     w = synthetic.WORKLOADS[wid]
     say("workload", w.name, "dtype", kv_dtype, "chunk", chunk or w.chunk)
     q = synthetic.gen_q(w)
@@ -188,10 +189,35 @@ def run_workload(orc, wid, kv_dtype=q8a.KV_Q8_0, chunk=None, rows_per_head=None)
         kb, vb = synthetic.to_f16_bits(k), synthetic.to_f16_bits(v)
         kd, vd = f16_to_dev(kb), f16_to_dev(vb)
         prob = orc.Problem(q, kb, vb, orc.KV_F16, w.q_pos0)
-    del k, v
     bc = chunk or w.chunk
-    out, lse, _ = prefill(qd, kd, vd, kv_dtype, w.B, w.H, w.M, w.N, w.q_pos0,
-                          [(s, min(bc, w.N - s)) for s in range(0, w.N, bc)])
+    chunks = [(s, min(bc, w.N - s)) for s in range(0, w.N, bc)]
+    if append:
+        # the tokens at positions >= q_pos0 arrive with the queries: their cache rows start
+        # out as junk and are written by attn_append_chunk from the FP32 values
+        assert w.B == 1 and chunks[-1][0] == w.q_pos0
+        kd[:, :, w.q_pos0:] = 0xA5
+        vd[:, :, w.q_pos0:] = 0xA5
+        chunks = chunks[:-1]
+        m, l, o = q8a.alloc_state(w.B, w.H, w.M)
+        st = q8a.attn_state_init(m, l, o, w.B, w.H, w.M, D, w.q_pos0)
+        prefill(qd, kd, vd, kv_dtype, w.B, w.H, w.M, w.N, w.q_pos0, chunks,
+                state=(st, (m, l, o)), finalize=False)
+        kn = torch.from_numpy(np.ascontiguousarray(k[:, :, w.q_pos0:])).to(dev())
+        vn = torch.from_numpy(np.ascontiguousarray(v[:, :, w.q_pos0:])).to(dev())
+        say("append", w.N - w.q_pos0, "tokens")
+        q8a.attn_append_chunk(st, qd, kn, vn, kd.data_ptr() + w.q_pos0 * 68,
+                              vd.data_ptr() + w.q_pos0 * 68, w.q_pos0, w.N - w.q_pos0,
+                              w.N * 68, w.H * w.N * 68, 1)
+        out = torch.empty((w.B, w.H, w.M, D), dtype=torch.float16, device=dev())
+        lse = torch.empty((w.B, w.H, w.M), dtype=torch.float32, device=dev())
+        q8a.attn_finalize(st, out, lse)
+        torch.cuda.synchronize()
+        assert np.array_equal(kd[:, :, w.q_pos0:].cpu().numpy(), kb[:, :, w.q_pos0:])
+        assert np.array_equal(vd[:, :, w.q_pos0:].cpu().numpy(), vb[:, :, w.q_pos0:])
+        del kn, vn
+    else:
+        out, lse, _ = prefill(qd, kd, vd, kv_dtype, w.B, w.H, w.M, w.N, w.q_pos0, chunks)
+    del k, v
     rows = synthetic.sample_rows(w, rows_per_head)
     O_ref, lse_ref = orc.attention(prob, rows)
     return assert_close(rows_of(out, rows, D), rows_of(lse, rows), O_ref, lse_ref, w.name)
@@ -222,4 +248,6 @@ def test_workload_batch8_one_chunk(orc):
 
 @pytest.mark.timeout(300)
 def test_workload_append_133k(orc):
-    run_workload(orc, 3)
+    """The 131,072 cached tokens through attn_accumulate_chunk, the 2048 appended tokens (the
+    queries' own positions) through attn_append_chunk from FP32."""
+    run_workload(orc, 3, append=True)
