@@ -167,6 +167,9 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
     torch.cuda.synchronize()
     ms_graph = t0.elapsed_time(t1) / steps
     graph_equal = graph_equal and bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse))
+    append = None
+    if (kv_dtype == q8a.KV_Q8_0 and w.q_pos0 > 0 and chunks[-1][0] == w.q_pos0 and w.B == 1):
+        append = measure_append(w, qd, kx, vx, kd, vd, m, l, o, out, lse, chunks, steps)
     acc_ms = [a.elapsed_time(b) for a, b in ev["accumulate"]]
     acc_mean_ms = float(np.mean(acc_ms))
     acc_flops_mean = float(np.mean(acc_flops))
@@ -175,8 +178,84 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
                acc_mean_ms=acc_mean_ms, acc_flops_mean=acc_flops_mean,
                acc_per_chunk_us=[1e3 * float(np.mean(acc_ms[i::len(chunks)]))
                                  for i in range(len(chunks))],
-               acc_flops=acc_flops, k=k, v=v, chunks=chunks)
+               acc_flops=acc_flops, k=k, v=v, chunks=chunks, append=append)
     return res
+
+
+def measure_append(w, qd, kx, vx, kd, vd, m, l, o, out, lse, chunks, steps):
+    """Quantise-on-append for a workload whose last chunk is the queries' own new tokens
+    (positions >= q_pos0): attn_append_chunk packs them from FP32 into their cache rows and
+    accumulates them.  Timed: the step init + calls over the cached tokens + the append call +
+    finalize; the append call alone on the resumed state (restored before every repetition);
+    and, for comparison, the same work as two q8_0_pack launches into a staging buffer plus one
+    attn_accumulate_chunk."""
+    import numpy as np
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+
+    n_new = w.N - w.q_pos0
+    kn = kx[:, :, w.q_pos0:].contiguous()
+    vn = vx[:, :, w.q_pos0:].contiguous()
+    kp = torch.empty((w.B, w.H, n_new, 68), dtype=torch.uint8, device=kx.device)
+    vp = torch.empty_like(kp)
+    hs, ss = w.N * 68, w.H * w.N * 68
+    koff, voff = kd.data_ptr() + w.q_pos0 * 68, vd.data_ptr() + w.q_pos0 * 68
+
+    def cached_part():
+        st = q8a.attn_state_init(m, l, o, w.B, w.H, w.M, w.D, w.q_pos0)
+        for s_, n_ in chunks[:-1]:
+            q8a.attn_accumulate_chunk(st, qd, kd.data_ptr() + s_ * 68, vd.data_ptr() + s_ * 68,
+                                      q8a.KV_Q8_0, s_, n_, hs, ss, 1)
+        return st
+
+    def fused(st):
+        q8a.attn_append_chunk(st, qd, kn, vn, koff, voff, w.q_pos0, n_new, hs, ss, 1)
+
+    def separate(st):
+        q8a.q8_0_pack(kn, kp, w.B * w.H * n_new, 64)
+        q8a.q8_0_pack(vn, vp, w.B * w.H * n_new, 64)
+        q8a.attn_accumulate_chunk(st, qd, kp, vp, q8a.KV_Q8_0, w.q_pos0, n_new, n_new * 68,
+                                  w.H * n_new * 68, 1)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the whole step with the append call
+    for _ in range(2):
+        fused(cached_part())
+        q8a.attn_finalize(cached_part(), out, lse)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        st = cached_part()
+        fused(st)
+        q8a.attn_finalize(st, out, lse)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / steps
+    # the append call alone, from the resumed state of the cached part
+    st = cached_part()
+    torch.cuda.synchronize()
+    m0, l0, o0 = m.clone(), l.clone(), o.clone()
+    times = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        d = []
+        for _ in range(steps + 2):
+            m.copy_(m0)
+            l.copy_(l0)
+            o.copy_(o0)
+            ev0.record()
+            fn(st)
+            ev1.record()
+            torch.cuda.synchronize()
+            d.append(ev0.elapsed_time(ev1))
+        times[name] = 1e3 * float(np.mean(d[2:]))
+    return {"new_tokens": n_new, "ms_per_step_with_append": round(ms_step, 4),
+            "append_call_us": round(times["fused"], 2),
+            "pack_pack_accumulate_us": round(times["separate"], 2),
+            "note": "step = init + %d calls over the cached tokens + attn_append_chunk of the "
+                    "%d new tokens from FP32 + finalize; the call alone runs on the restored "
+                    "resumed state; the comparison packs into a staging buffer (two launches) "
+                    "and accumulates from it" % (len(chunks) - 1, n_new)}
 
 
 def build_streamed_cache(w):
@@ -649,6 +728,8 @@ def main():
         "kernels": res["kernels"],
         "accumulate_us_per_chunk": [round(x, 3) for x in res["acc_per_chunk_us"]],
     }
+    if res["append"]:
+        line["append"] = res["append"]
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, res, kv_dtype, args.cpu_seconds)
         line["cpu_baseline"] = base
