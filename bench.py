@@ -386,7 +386,7 @@ def burst_line(w, args):
     print(json.dumps(line), flush=True)
 
 
-def run_streamed(w, steps, warmup):
+def run_streamed(w, steps, warmup, feed_dir=None):
     """The 1M-token workload: Q8_0 K and V in pinned host memory, chunk-major, streamed through
     two device slots per tensor by attn_accumulate_stream (copies on a side stream, compute on
     the current stream).  Also timed: the same chunk calls over a device-resident copy of the
@@ -451,12 +451,82 @@ def run_streamed(w, steps, warmup):
     ms_resident = timed(resident)
     same = bool(torch.equal(out_stream, out))
     ms_copy = timed(copies)
+    feed = None
+    if feed_dir:
+        feed = file_feed(w, feed_dir, qd, kh, vh, m, l, o, out, out_stream, slots_k, slots_v,
+                         chunk_bytes, cur, copy_stream)
     return dict(ms_stream=ms_stream, ms_resident=ms_resident, ms_copy=ms_copy,
-                streamed_equals_resident=same, kv_bytes=2 * C * chunk_bytes)
+                streamed_equals_resident=same, kv_bytes=2 * C * chunk_bytes, file_feed=feed)
+
+
+def file_feed(w, feed_dir, qd, kh, vh, m, l, o, out, out_stream, slots_k, slots_v, chunk_bytes,
+              cur, copy_stream, steps=3):
+    """The same workload fed from storage: the chunk-major K and V written to two files (then
+    dropped from the page cache), read back with O_DIRECT by attn_accumulate_file into a pinned
+    two-slot ring.  Timed on the host clock (the call blocks until every chunk is read).  Also
+    the raw O_DIRECT read rate of the two files into the ring, without the GPU."""
+    import time
+
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+
+    H, chunk = w.H, w.chunk
+    paths = [os.path.join(feed_dir, "q8a_feed_%d_%s.bin" % (os.getpid(), t)) for t in "kv"]
+    ring_bytes = chunk_bytes + 8192
+    # direct reads cannot land in pinned memory: the ring is anonymous mmap memory
+    ring_k, ring_v = q8a.alloc_ring(ring_bytes), q8a.alloc_ring(ring_bytes)
+    try:
+        for pth, src in zip(paths, (kh, vh)):
+            with open(pth, "wb") as f:
+                src.numpy().reshape(-1).tofile(f)
+                f.flush()
+                os.fsync(f.fileno())
+            fd = os.open(pth, os.O_RDONLY)
+            os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+            os.close(fd)
+        fds = [os.open(pth, os.O_RDONLY | os.O_DIRECT) for pth in paths]
+        try:
+            # raw read rate: the files into the ring, chunk by chunk, no GPU
+            t0 = time.perf_counter()
+            for c in range(w.n_chunks):
+                for fd, ring in zip(fds, (ring_k, ring_v)):
+                    view = memoryview(ring[c & 1])[:chunk_bytes]
+                    got = os.preadv(fd, [view], c * chunk_bytes)
+                    assert got == chunk_bytes
+            t_raw = time.perf_counter() - t0
+            res = []
+            for i in range(steps + 1):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                st = q8a.attn_state_init(m, l, o, 1, H, w.M, w.D, w.q_pos0, cur)
+                q8a.attn_accumulate_file(st, qd, fds[0], fds[1], 0, q8a.KV_Q8_0, w.N, chunk,
+                                         ring_k, ring_v, ring_bytes, slots_k, slots_v, 1, cur,
+                                         copy_stream)
+                q8a.attn_finalize(st, out, None, cur)
+                torch.cuda.synchronize()
+                if i:
+                    res.append(time.perf_counter() - t0)
+            same = bool(torch.equal(out, out_stream))
+        finally:
+            for fd in fds:
+                os.close(fd)
+    finally:
+        for pth in paths:
+            if os.path.exists(pth):
+                os.unlink(pth)
+    kv = 2 * w.n_chunks * chunk_bytes
+    ms = 1e3 * sum(res) / len(res)
+    return {"ms_per_step": round(ms, 2), "kv_gbps": round(kv / (ms * 1e-3) / 1e9, 3),
+            "storage_read_gbps_odirect": round(kv / t_raw / 1e9, 3),
+            "equals_streamed": same, "steps": steps,
+            "note": "step = init + attn_accumulate_file + finalize, host clock; files in %s "
+                    "opened with O_DIRECT, read with pread into a two-slot ring of mmap'd memory; "
+                    "storage_read_gbps: the same reads without the GPU" % feed_dir}
 
 
 def streamed_line(w, args):
-    r = run_streamed(w, args.steps, args.warmup)
+    r = run_streamed(w, args.steps, args.warmup, args.feed_dir)
     flops = w.visible_pairs() * 4 * w.D
     kv = r["kv_bytes"]
     line = {
@@ -479,6 +549,7 @@ def streamed_line(w, args):
         "h2d_gbps_copy_only": round(kv / (r["ms_copy"] * 1e-3) / 1e9, 3),
         "overlap_efficiency": round(max(r["ms_copy"], r["ms_resident"]) / r["ms_stream"], 4),
         "streamed_equals_resident": r["streamed_equals_resident"],
+        "file_feed": r["file_feed"],
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -637,6 +708,9 @@ def main():
                     help="0-3: resident workloads; 4: the streamed 1M-token workload; "
                          "5: Mode B burst verification over the 1M-token cache")
     ap.add_argument("--chunk", type=int, default=None, help="override B_C")
+    ap.add_argument("--feed-dir", default=None,
+                    help="workload 4: also feed the cache from files in this directory "
+                         "(attn_accumulate_file, O_DIRECT)")
     ap.add_argument("--kv", choices=["q8_0", "f16"], default="q8_0")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -28,6 +28,7 @@ Q8A_E_UNSUPPORTED = 2
 Q8A_E_ALIGN = 3
 Q8A_E_STATE = 4
 Q8A_E_HIP = 5
+Q8A_E_IO = 6
 KV_Q8_0 = 0
 KV_F16 = 1
 STATE_MAGIC = 0x51384154
@@ -36,7 +37,8 @@ ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
 
 EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_append_chunk",
            "attn_finalize",
-           "attn_state_merge", "attn_accumulate_stream", "q8a_status_string",
+           "attn_state_merge", "attn_accumulate_stream", "attn_accumulate_file",
+           "q8a_status_string",
            "q8a_last_hip_error")
 
 
@@ -81,12 +83,16 @@ def library() -> ctypes.CDLL:
     lib.attn_state_merge.argtypes = [SP, SP, P]
     lib.attn_accumulate_stream.argtypes = [SP, P, P, P, i32, i64, i32, ctypes.POINTER(P),
                                            ctypes.POINTER(P), i32, P, P]
+    lib.attn_accumulate_file.argtypes = [SP, P, ctypes.c_int, ctypes.c_int, i64, i32, i64, i32,
+                                         ctypes.POINTER(P), ctypes.POINTER(P), i64,
+                                         ctypes.POINTER(P), ctypes.POINTER(P), i32, P, P]
     lib.q8a_status_string.restype = ctypes.c_char_p
     lib.q8a_status_string.argtypes = [ctypes.c_int]
     lib.q8a_last_hip_error.restype = ctypes.c_int
     lib.q8a_last_hip_error.argtypes = []
     for name in ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_append_chunk",
-                 "attn_finalize", "attn_state_merge", "attn_accumulate_stream"):
+                 "attn_finalize", "attn_state_merge", "attn_accumulate_stream",
+                 "attn_accumulate_file"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -106,6 +112,8 @@ def _ptr(x) -> int | None:
         return None
     if isinstance(x, torch.Tensor):
         return x.data_ptr()
+    if hasattr(x, "__array_interface__"):  # a numpy array (e.g. an mmap'd ring buffer)
+        return x.__array_interface__["data"][0]
     return int(x)
 
 
@@ -173,6 +181,41 @@ def attn_accumulate_stream(st: q8a_state, q, k_host, v_host, kv_dtype: int, n_kv
                                             _ptr(v_host), int(kv_dtype), int(n_kv_total),
                                             int(chunk_tokens), sk, sv, int(causal),
                                             _stream(compute_stream), _stream(copy_stream)))
+
+
+def attn_accumulate_file(st: q8a_state, q, fd_k: int, fd_v: int, file_offset: int, kv_dtype: int,
+                         n_kv_total: int, chunk_tokens: int, ring_k, ring_v, ring_bytes: int,
+                         slot_k, slot_v, causal: int = 1, compute_stream=None,
+                         copy_stream=None) -> None:
+    """Stream a chunk-major KV cache from two files (pread into a pinned two-slot ring, then
+    through two device slots per tensor); blocks the host until every chunk has been read."""
+    rk = (ctypes.c_void_p * 2)(_ptr(ring_k[0]), _ptr(ring_k[1]))
+    rv = (ctypes.c_void_p * 2)(_ptr(ring_v[0]), _ptr(ring_v[1]))
+    sk = (ctypes.c_void_p * 2)(_ptr(slot_k[0]), _ptr(slot_k[1]))
+    sv = (ctypes.c_void_p * 2)(_ptr(slot_v[0]), _ptr(slot_v[1]))
+    _check(library().attn_accumulate_file(ctypes.byref(st), _ptr(q), int(fd_k), int(fd_v),
+                                          int(file_offset), int(kv_dtype), int(n_kv_total),
+                                          int(chunk_tokens), rk, rv, int(ring_bytes), sk, sv,
+                                          int(causal), _stream(compute_stream),
+                                          _stream(copy_stream)))
+
+
+def alloc_ring(n_bytes: int, pinned: bool = False):
+    """Convenience: the two 4096-byte-aligned host buffers of n_bytes of attn_accumulate_file's
+    ring; anonymous mmap memory (for O_DIRECT descriptors, which cannot read into pinned memory)
+    or pinned memory (for buffered descriptors)."""
+    import mmap
+
+    import numpy as np
+    out = []
+    for _ in range(2):
+        if pinned:
+            t = torch.empty(n_bytes + 4096, dtype=torch.uint8, pin_memory=True)
+            pad = (-t.data_ptr()) % 4096
+            out.append(t[pad:pad + n_bytes])
+        else:
+            out.append(np.frombuffer(mmap.mmap(-1, n_bytes), dtype=np.uint8))
+    return out
 
 
 def sub_state(st: q8a_state, s0: int, n: int) -> q8a_state:

@@ -1,7 +1,11 @@
 // C ABI of libq8attn.so: argument validation, launch configuration and the double-buffered
 // host-to-device streaming loop.  Every check runs before anything is enqueued; on failure the
 // state descriptor is left as it was.
+#include <errno.h>
 #include <stdint.h>
+#include <unistd.h>
+
+#include <thread>
 
 #include "q8attn.h"
 #include "q8attn_internal.h"
@@ -106,6 +110,7 @@ const char *q8a_status_string(int status)
     case Q8A_E_ALIGN: return "misaligned pointer or stride";
     case Q8A_E_STATE: return "state descriptor not initialised or inconsistent";
     case Q8A_E_HIP: return "HIP runtime error";
+    case Q8A_E_IO: return "file read failed or file too short";
     default: return "unknown status";
     }
 }
@@ -348,3 +353,167 @@ int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_hos
 }
 
 } // extern "C"
+
+namespace {
+
+// The 4096-byte-aligned range covering [off, off + len): pread over it (O_DIRECT needs aligned
+// offsets, sizes and buffers); the file may end inside the rounded tail, not before off + len.
+bool read_aligned(int fd, uint8_t *buf, int64_t off, int64_t len)
+{
+    const int64_t a0 = off & ~(int64_t)4095;
+    const int64_t want = ((off + len + 4095) & ~(int64_t)4095) - a0;
+    const int64_t need = off + len - a0;
+    int64_t got = 0;
+    while (got < need) {
+        const ssize_t r = pread(fd, buf + got, (size_t)(want - got), (off_t)(a0 + got));
+        if (r < 0) {
+            if (errno == EINTR)
+                continue;
+            return false;
+        }
+        if (r == 0)
+            break; // end of file
+        got += r;
+    }
+    return got >= need;
+}
+
+} // namespace
+
+int attn_accumulate_file(const q8a_state *st, const void *q, int fd_k, int fd_v,
+                         int64_t file_offset, int32_t kv_dtype, int64_t n_kv_total,
+                         int32_t chunk_tokens, void *const ring_k[2], void *const ring_v[2],
+                         int64_t ring_bytes, void *const slot_k[2], void *const slot_v[2],
+                         int32_t causal, void *compute_stream, void *copy_stream)
+{
+    if (!slot_k || !slot_v || !ring_k || !ring_v || n_kv_total < 1 || chunk_tokens < 1 ||
+        fd_k < 0 || fd_v < 0 || file_offset < 0)
+        return Q8A_E_INVAL;
+    for (int s = 0; s < 2; ++s)
+        if (!slot_k[s] || !slot_v[s] || !ring_k[s] || !ring_v[s])
+            return Q8A_E_INVAL;
+    if (st && st->magic == Q8A_STATE_MAGIC && n_kv_total > INT64_MAX / 4)
+        return Q8A_E_INVAL;
+    const int row = row_bytes(kv_dtype);
+    const int64_t head_stride = (int64_t)chunk_tokens * row;
+    int rc = check_chunk(st, q, slot_k[0], slot_v[0], kv_dtype, 0, chunk_tokens, head_stride,
+                         head_stride * (st ? st->n_heads : 1), causal);
+    if (rc)
+        return rc;
+    for (int s = 0; s < 2; ++s) {
+        if (!aligned(slot_k[s], 16) || !aligned(slot_v[s], 16))
+            return Q8A_E_ALIGN;
+        if (!aligned(ring_k[s], 4096) || !aligned(ring_v[s], 4096))
+            return Q8A_E_ALIGN;
+    }
+    const int64_t seq_stride = head_stride * st->n_heads;
+    const int64_t chunk_bytes = seq_stride * st->n_seq;
+    if (ring_bytes < chunk_bytes + 8192)
+        return Q8A_E_INVAL;
+    const int64_t n_chunks = (n_kv_total + chunk_tokens - 1) / chunk_tokens;
+    if (file_offset > INT64_MAX / 2 || n_chunks > (INT64_MAX / 2) / chunk_bytes)
+        return Q8A_E_INVAL;
+    hipStream_t cs = static_cast<hipStream_t>(compute_stream);
+    hipStream_t ds = static_cast<hipStream_t>(copy_stream);
+
+    hipEvent_t ev_full[2] = {nullptr, nullptr}, ev_free[2] = {nullptr, nullptr};
+    hipEvent_t ev_start = nullptr;
+    hipError_t e = hipSuccess;
+    int status = Q8A_OK;
+    auto destroy = [&]() {
+        for (int s = 0; s < 2; ++s) {
+            if (ev_full[s]) (void)hipEventDestroy(ev_full[s]);
+            if (ev_free[s]) (void)hipEventDestroy(ev_free[s]);
+        }
+        if (ev_start) (void)hipEventDestroy(ev_start);
+    };
+    for (int s = 0; s < 2 && e == hipSuccess; ++s) {
+        e = hipEventCreateWithFlags(&ev_full[s], hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&ev_free[s], hipEventDisableTiming);
+    }
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&ev_start, hipEventDisableTiming);
+    // the slots may still be read by earlier work on the compute stream
+    if (e == hipSuccess)
+        e = hipEventRecord(ev_start, cs);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(ds, ev_start, 0);
+    // chunk c of both files into ring slot s: K on this thread, V on a second one (or here
+    // too, should a thread not start)
+    auto read_chunk = [&](int64_t c, int s) -> bool {
+        const int64_t off = file_offset + c * chunk_bytes;
+        bool ok_v = false;
+        auto read_v = [&] {
+            ok_v = read_aligned(fd_v, static_cast<uint8_t *>(ring_v[s]), off, chunk_bytes);
+        };
+        std::thread tv;
+        try {
+            tv = std::thread(read_v);
+        } catch (...) {
+            read_v();
+        }
+        const bool ok_k = read_aligned(fd_k, static_cast<uint8_t *>(ring_k[s]), off,
+                                       chunk_bytes);
+        if (tv.joinable())
+            tv.join();
+        return ok_k && ok_v;
+    };
+    if (e == hipSuccess && !read_chunk(0, 0))
+        status = Q8A_E_IO;
+    for (int64_t c = 0; c < n_chunks && e == hipSuccess && status == Q8A_OK; ++c) {
+        const int s = (int)(c & 1);
+        const int64_t kv_pos0 = c * chunk_tokens;
+        const int32_t n_kv = (int32_t)((n_kv_total - kv_pos0) < chunk_tokens
+                                           ? (n_kv_total - kv_pos0) : chunk_tokens);
+        // chunk c+1 is read into the other slot while chunk c is copied and accumulated; that
+        // slot was last copied from for chunk c-1, whose copies must have completed
+        const bool has_next = c + 1 < n_chunks;
+        bool next_ok = true;
+        std::thread reader;
+        if (has_next) {
+            if (c >= 1)
+                e = hipEventSynchronize(ev_full[s ^ 1]);
+            if (e != hipSuccess)
+                break;
+            try {
+                reader = std::thread([&, c, s] { next_ok = read_chunk(c + 1, s ^ 1); });
+            } catch (...) {
+                next_ok = read_chunk(c + 1, s ^ 1); // no overlap, same result
+            }
+        }
+        const int64_t delta = (file_offset + c * chunk_bytes) & 4095;
+        const uint8_t *rk = static_cast<const uint8_t *>(ring_k[s]);
+        const uint8_t *rv = static_cast<const uint8_t *>(ring_v[s]);
+        if (c >= 2)
+            e = hipStreamWaitEvent(ds, ev_free[s], 0); // chunk c-2 has finished with slot s
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(slot_k[s], rk + delta, (size_t)chunk_bytes,
+                               hipMemcpyHostToDevice, ds);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(slot_v[s], rv + delta, (size_t)chunk_bytes,
+                               hipMemcpyHostToDevice, ds);
+        if (e == hipSuccess)
+            e = hipEventRecord(ev_full[s], ds);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(cs, ev_full[s], 0);
+        if (e == hipSuccess) {
+            q8a::AccumulateArgs a = make_args(st, q, slot_k[s], slot_v[s], kv_pos0, n_kv,
+                                              head_stride, seq_stride, causal);
+            e = q8a::launch_accumulate(a, kv_dtype, cs);
+        }
+        if (e == hipSuccess)
+            e = hipEventRecord(ev_free[s], cs);
+        if (reader.joinable())
+            reader.join();
+        if (!next_ok)
+            status = Q8A_E_IO;
+    }
+    // the ring buffers are free once their last copies have completed
+    for (int s = 0; s < 2 && e == hipSuccess && n_chunks > s; ++s)
+        e = hipEventSynchronize(ev_full[s]);
+    destroy();
+    if (e != hipSuccess)
+        return hip_failure(e);
+    return status;
+}

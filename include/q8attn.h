@@ -42,7 +42,8 @@ typedef enum {
     Q8A_E_UNSUPPORTED = 2, /* a valid request this library does not implement (e.g. head_dim) */
     Q8A_E_ALIGN = 3,       /* a pointer or stride breaks the stated alignment */
     Q8A_E_STATE = 4,       /* descriptor not initialised, or it does not match the call */
-    Q8A_E_HIP = 5          /* a HIP runtime call failed; see q8a_last_hip_error() */
+    Q8A_E_HIP = 5,         /* a HIP runtime call failed; see q8a_last_hip_error() */
+    Q8A_E_IO = 6           /* a file read failed or the file ended early (attn_accumulate_file) */
 } q8a_status;
 
 typedef enum {
@@ -164,6 +165,35 @@ int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_hos
                            const void *v_host, int32_t kv_dtype, int64_t n_kv_total,
                            int32_t chunk_tokens, void *const slot_k[2], void *const slot_v[2],
                            int32_t causal, void *compute_stream, void *copy_stream);
+
+/* Out-of-core feed from storage ("Out-of-Core Flash Streaming ...", Sec. 2: KV chunks read from
+ * flash with the page cache bypassed into a two-slot ring, then consumed by the GPU): the same
+ * work as attn_accumulate_stream, with the chunk-major K and V read from files.
+ *   fd_k, fd_v   open file descriptors (the caller opens them, with O_DIRECT to bypass the page
+ *                cache); each holds the layout attn_accumulate_stream takes from host memory,
+ *                [chunk][n_seq][n_heads][chunk_tokens][row], starting at byte file_offset
+ *                (>= 0), the last chunk padded to full size or ending the file.
+ *   ring_k, ring_v  two host buffers each, 4096-byte aligned, ring_bytes long, ring_bytes >=
+ *                chunk bytes + 8192: each chunk is read with pread over the 4096-byte-aligned
+ *                range that covers it (what O_DIRECT needs), then copied to the device from
+ *                inside that range.  With O_DIRECT descriptors the ring must be ordinary
+ *                page-aligned memory (an anonymous mmap, for example): direct reads into pinned
+ *                (hipHostMalloc) memory fail with EFAULT, and the device copy then stages the
+ *                pageable buffer.  With buffered descriptors a pinned ring gives asynchronous
+ *                copies.
+ *   slot_k, slot_v, q, kv_dtype, n_kv_total, chunk_tokens, causal, streams: as for
+ *                attn_accumulate_stream.
+ * The call blocks the host: chunk c+1 is read while chunk c is copied (copy_stream) and
+ * accumulated (compute_stream); a ring buffer is refilled only after its previous copy has
+ * completed.  On return every chunk has been read and its work enqueued, and the ring buffers
+ * are no longer in use; compute_stream carries the completion of the last chunk.
+ * Q8A_E_IO: a read failed or a file ended early; the chunks before it have been accumulated
+ * (their work is enqueued), so the state then holds a prefix of the keys. */
+int attn_accumulate_file(const q8a_state *st, const void *q, int fd_k, int fd_v,
+                         int64_t file_offset, int32_t kv_dtype, int64_t n_kv_total,
+                         int32_t chunk_tokens, void *const ring_k[2], void *const ring_v[2],
+                         int64_t ring_bytes, void *const slot_k[2], void *const slot_v[2],
+                         int32_t causal, void *compute_stream, void *copy_stream);
 
 /* Human-readable name of a q8a_status value. */
 const char *q8a_status_string(int status);

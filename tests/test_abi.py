@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert q8a.status_string(0) == "ok"
-    for s in range(1, 6):
+    for s in range(1, 7):
         assert q8a.status_string(s) != "unknown status"
     assert q8a.status_string(99) == "unknown status"
 
@@ -211,6 +211,32 @@ def test_stream_rejects_bad_arguments():
     assert call(q8a.q8a_state(), slots, slots) == q8a.Q8A_E_STATE
     assert call(st, slots, slots, dtype=3) == q8a.Q8A_E_INVAL
     assert call(st, (P * 2)(A16B, A16C + 8), slots) == q8a.Q8A_E_ALIGN
+
+
+def test_file_feed_rejects_bad_arguments():
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    st = fake_state(H=2, M=64)
+    chunk = 256
+    cb = 2 * chunk * 68                       # chunk bytes (one sequence, two heads)
+    slots = (P * 2)(A16B, A16C)
+    ring = (P * 2)(0x1000000, 0x2000000)      # 4096-aligned fake host addresses
+    ring2 = (P * 2)(0x3000000, 0x4000000)
+
+    def call(st_=st, fk=3, fv=4, off=0, rk=ring, rv=ring2, rb=cb + 8192, sk=slots, sv=slots,
+             n_total=1000, dtype=0):
+        return lib.attn_accumulate_file(ctypes.byref(st_), P(A16), fk, fv, off, dtype, n_total,
+                                        chunk, rk, rv, rb, sk, sv, 1, None, None)
+    assert call(fk=-1) == q8a.Q8A_E_INVAL
+    assert call(fv=-5) == q8a.Q8A_E_INVAL
+    assert call(off=-1) == q8a.Q8A_E_INVAL
+    assert call(n_total=0) == q8a.Q8A_E_INVAL
+    assert call(rk=(P * 2)(0x1000000, None)) == q8a.Q8A_E_INVAL
+    assert call(rb=cb + 8191) == q8a.Q8A_E_INVAL             # no room for the aligned read
+    assert call(rv=(P * 2)(0x3000000, 0x4000000 + 2048)) == q8a.Q8A_E_ALIGN
+    assert call(sk=(P * 2)(A16B, A16C + 8)) == q8a.Q8A_E_ALIGN
+    assert call(st_=q8a.q8a_state()) == q8a.Q8A_E_STATE
+    assert call(dtype=4) == q8a.Q8A_E_INVAL
 
 
 @pytest.mark.skipif(not NO_GPU, reason="needs a host without a GPU")
