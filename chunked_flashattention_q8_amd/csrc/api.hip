@@ -22,6 +22,10 @@ int hip_failure(hipError_t e)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// query rows per (sequence, head): a head's O rows (256 bytes each) are addressed with 32-bit
+// byte offsets
+constexpr int32_t kMaxRows = (1 << 24) - 1;
+
 int row_bytes(int32_t kv_dtype)
 {
     return kv_dtype == Q8A_KV_Q8_0 ? q8a::kQ8RowBytes
@@ -66,7 +70,7 @@ int check_chunk(const q8a_state *st, const void *q, const void *k, const void *v
         return Q8A_E_INVAL;
     if (st->n_seq > 1 && seq_stride < (int64_t)n_kv * row)
         return Q8A_E_INVAL;
-    if (st->n_heads > 65535 || st->n_seq > 65535)
+    if (st->n_heads > 65535 || st->n_seq > 65535 || st->n_q > kMaxRows)
         return Q8A_E_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || head_stride % 16 ||
         seq_stride % 16)
@@ -143,7 +147,8 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
         return Q8A_E_INVAL;
     if (head_dim != q8a::kHeadDim)
         return Q8A_E_UNSUPPORTED;
-    if (n_heads > 65535 || n_seq > 65535 || (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 36))
+    if (n_heads > 65535 || n_seq > 65535 || n_q > kMaxRows ||
+        (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 36))
         return Q8A_E_UNSUPPORTED;
     if (!aligned(m, 4) || !aligned(l, 4) || !aligned(o, 16))
         return Q8A_E_ALIGN;
@@ -212,10 +217,18 @@ int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
         const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
         return x < y + nb && y < x + na;
     };
+    // ... nor Q or the state, which the accumulate reads after the pack has written
+    const int64_t rows = state_rows(st);
+    const void *reads[5] = {k_new, v_new, q, st->m, st->l};
+    const int64_t spans[5] = {src_span, src_span, rows * q8a::kHeadDim * 2, rows * 4, rows * 4};
     if (overlap(k_cache, dst_span, v_cache, dst_span) ||
-        overlap(k_cache, dst_span, k_new, src_span) || overlap(k_cache, dst_span, v_new, src_span) ||
-        overlap(v_cache, dst_span, k_new, src_span) || overlap(v_cache, dst_span, v_new, src_span))
+        overlap(k_cache, dst_span, st->o, rows * q8a::kHeadDim * 4) ||
+        overlap(v_cache, dst_span, st->o, rows * q8a::kHeadDim * 4))
         return Q8A_E_INVAL;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(k_cache, dst_span, reads[i], spans[i]) ||
+            overlap(v_cache, dst_span, reads[i], spans[i]))
+            return Q8A_E_INVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = q8a::launch_q8_0_pack_rows(k_new, v_new, static_cast<uint8_t *>(k_cache),
                                               static_cast<uint8_t *>(v_cache), st->n_seq,

@@ -83,7 +83,9 @@ int q8_0_pack(const float *x, void *dst, int64_t n_rows, int32_t row_len, void *
 /* Describe a state and make every row empty: writes m = -inf and l = 0 for all
  * n_seq*n_heads*n_q rows (O is not written; see q8a_state).
  *   m, l    FP32 [n_seq][n_heads][n_q], 4-byte aligned;  o  FP32 [...][64], 16-byte aligned.
- *   head_dim must be 64 (else Q8A_E_UNSUPPORTED); n_seq, n_heads, n_q >= 1; q_pos0 >= 0. */
+ *   head_dim must be 64 (else Q8A_E_UNSUPPORTED); n_seq, n_heads, n_q >= 1; q_pos0 >= 0.
+ *   n_seq, n_heads <= 65535, n_q <= 16,777,215 (a head's O rows are addressed with 32-bit byte
+ *   offsets) and n_seq*n_heads*n_q <= 2^36, else Q8A_E_UNSUPPORTED. */
 int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
                     int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0,
                     void *stream);
@@ -123,7 +125,9 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
  *            2^46 bytes.  With several sequences and several heads, the (sequence, head) runs must
  *            not interleave: kv_seq_stride >= (n_heads-1)*kv_head_stride + n_kv*68, or the same
  *            with the roles swapped.  The K and V destinations must not overlap each other or
- *            the FP32 sources (Q8A_E_INVAL).  Only the n_kv*68 bytes of each run are written.
+ *            the FP32 sources, Q or the state (Q8A_E_INVAL).  Only the n_kv*68 bytes of each run
+ *            are written; should the accumulate launch fail (Q8A_E_HIP), the cache rows are
+ *            written and the state is not.
  *   q, kv_pos0, n_kv, causal, stream: as for attn_accumulate_chunk.
  * Two launches on the stream (one pack of both tensors, one accumulate). */
 int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,

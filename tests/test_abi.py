@@ -77,6 +77,8 @@ def test_state_init_rejects_bad_arguments():
     assert lib.attn_state_init(ctypes.byref(st), P(A16), P(A16B), P(A16C + 8), 1, 4, 256, 64,
                                0, None) == q8a.Q8A_E_ALIGN
     assert lib.attn_state_init(None, *ok, 1, 4, 256, 64, 0, None) == q8a.Q8A_E_INVAL
+    assert lib.attn_state_init(ctypes.byref(st), *ok, 1, 1, 1 << 24, 64, 0, None) == \
+        q8a.Q8A_E_UNSUPPORTED                                  # beyond 32-bit row offsets
     assert st.magic == 0  # untouched on failure
 
 
@@ -151,6 +153,10 @@ def test_append_rejects_bad_arguments():
     assert append(st2, hs=64 * 68, ss=0) == q8a.Q8A_E_INVAL
     big = fake_state(B=300, H=300)
     assert append(big, hs=64 * 68, ss=300 * 64 * 68) == q8a.Q8A_E_UNSUPPORTED
+    assert append(st, kc=A16) == q8a.Q8A_E_INVAL                # over Q (and the state's m)
+    assert append(st, vc=A16C) == q8a.Q8A_E_INVAL               # over the state's O
+    tall = fake_state(H=1, M=1 << 24)
+    assert acc(tall) == q8a.Q8A_E_UNSUPPORTED
 
 
 @pytest.mark.skipif(not NO_GPU, reason="needs a host without a GPU")
