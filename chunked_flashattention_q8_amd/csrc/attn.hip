@@ -450,12 +450,15 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(a.o + head * a.M * kHeadDim,
                                                   (uint32_t)a.M * kHeadDim * 4u);
     const __amdgpu_buffer_rsrc_t rs_l = make_rsrc(a.l + head * a.M, (uint32_t)a.M * 4u);
+    // past-the-end offset: beyond the largest range (n_q < 2^24 rows of 256 bytes, checked on
+    // the host) even with the 240 bytes a row's last piece adds, and without wrapping
+    constexpr uint32_t kNoRow = 0xFFFFFF00u;
     auto load_resumed = [&]() {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const bool res = m_old[j] != -INFINITY;
-            const uint32_t ob = res ? (uint32_t)qi[j] * (kHeadDim * 4u) : 0x80000000u;
-            const uint32_t lb = (res && g == 0) ? (uint32_t)qi[j] * 4u : 0x80000000u;
+            const uint32_t ob = res ? (uint32_t)qi[j] * (kHeadDim * 4u) : kNoRow;
+            const uint32_t lb = (res && g == 0) ? (uint32_t)qi[j] * 4u : kNoRow;
             l_part[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_l, lb, 0, 0));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
