@@ -129,7 +129,7 @@ int q8_0_pack(const float *x, void *dst, int64_t n_rows, int32_t row_len, void *
         return Q8A_OK;
     if (!x || !dst)
         return Q8A_E_INVAL;
-    if (n_rows > ((int64_t)1 << 36) / (row_len / 32)) // grid and index ranges
+    if (n_rows > ((int64_t)1 << 28) / (row_len / 32)) // 8 lanes per block: < 2^32 work-items
         return Q8A_E_INVAL;
     if (!aligned(x, 16) || !aligned(dst, 2))
         return Q8A_E_ALIGN;
@@ -147,8 +147,11 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
         return Q8A_E_INVAL;
     if (head_dim != q8a::kHeadDim)
         return Q8A_E_UNSUPPORTED;
+    // launches stay below 2^32 work-items: 8 lanes per state row in finalize and merge, one
+    // 256-thread workgroup per 256 rows of each (sequence, head) in accumulate
     if (n_heads > 65535 || n_seq > 65535 || n_q > kMaxRows ||
-        (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 36))
+        (int64_t)n_seq * n_heads > ((int64_t)1 << 23) ||
+        (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 28))
         return Q8A_E_UNSUPPORTED;
     if (!aligned(m, 4) || !aligned(l, 4) || !aligned(o, 16))
         return Q8A_E_ALIGN;

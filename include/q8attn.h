@@ -74,7 +74,8 @@ typedef struct {
  *   x       FP32 [n_rows][row_len], C-contiguous, 16-byte aligned.
  *   dst     n_rows * row_len/32 * 34 bytes, 2-byte aligned; block k of the flat sequence at byte
  *           34*k: the FP16 scale (little-endian) then 32 int8.
- *   row_len positive multiple of 32 (64 for a KV head row); n_rows >= 0 (0 enqueues nothing).
+ *   row_len positive multiple of 32 (64 for a KV head row); n_rows >= 0 (0 enqueues nothing);
+ *           at most 2^28 blocks per call (else Q8A_E_INVAL).
  * Per block: amax = max|x|, d = amax/127 (FP32, correctly rounded), d16 = FP16(d) (round to
  * nearest even), q = round(x / d16) (FP32 division, halves away from zero), clamped to
  * [-127, 127]; an all-zero block stores d16 = 0 and q = 0.  Bit-exact with the CPU oracle. */
@@ -85,7 +86,8 @@ int q8_0_pack(const float *x, void *dst, int64_t n_rows, int32_t row_len, void *
  *   m, l    FP32 [n_seq][n_heads][n_q], 4-byte aligned;  o  FP32 [...][64], 16-byte aligned.
  *   head_dim must be 64 (else Q8A_E_UNSUPPORTED); n_seq, n_heads, n_q >= 1; q_pos0 >= 0.
  *   n_seq, n_heads <= 65535, n_q <= 16,777,215 (a head's O rows are addressed with 32-bit byte
- *   offsets) and n_seq*n_heads*n_q <= 2^36, else Q8A_E_UNSUPPORTED. */
+ *   offsets), n_seq*n_heads <= 2^23 and n_seq*n_heads*n_q <= 2^28 (every launch stays below 2^32
+ *   work-items), else Q8A_E_UNSUPPORTED. */
 int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
                     int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0,
                     void *stream);

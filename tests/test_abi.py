@@ -62,6 +62,7 @@ def test_pack_rejects_bad_arguments():
     assert lib.q8_0_pack(P(A16 + 4), P(A16B), 4, 64, None) == q8a.Q8A_E_ALIGN
     assert lib.q8_0_pack(P(A16), P(A16B + 1), 4, 64, None) == q8a.Q8A_E_ALIGN
     assert lib.q8_0_pack(P(A16), P(A16B), 0, 64, None) == q8a.Q8A_OK  # nothing to do
+    assert lib.q8_0_pack(P(A16), P(A16B), (1 << 27) + 1, 64, None) == q8a.Q8A_E_INVAL
 
 
 def test_state_init_rejects_bad_arguments():
@@ -79,6 +80,10 @@ def test_state_init_rejects_bad_arguments():
     assert lib.attn_state_init(None, *ok, 1, 4, 256, 64, 0, None) == q8a.Q8A_E_INVAL
     assert lib.attn_state_init(ctypes.byref(st), *ok, 1, 1, 1 << 24, 64, 0, None) == \
         q8a.Q8A_E_UNSUPPORTED                                  # beyond 32-bit row offsets
+    assert lib.attn_state_init(ctypes.byref(st), *ok, 4096, 4096, 1, 64, 0, None) == \
+        q8a.Q8A_E_UNSUPPORTED                                  # 2^24 (sequence, head) pairs
+    assert lib.attn_state_init(ctypes.byref(st), *ok, 64, 64, 1 << 17, 64, 0, None) == \
+        q8a.Q8A_E_UNSUPPORTED                                  # 2^29 rows
     assert st.magic == 0  # untouched on failure
 
 
