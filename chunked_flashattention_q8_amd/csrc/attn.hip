@@ -28,9 +28,14 @@
 //     rarely rescaled; the state written back is renormalised to the true running maximum.
 //   * Tiles wholly above the causal diagonal are skipped ("Core Architecture ...", Sec. 5,
 //     causal skipping); rows that see no key of the chunk are not written.
-//   * A state row whose m is -inf is empty: its O and l are not read.
+//   * A state row whose m is -inf is empty: its O and l are not read.  The first two tiles'
+//     copies, Q and m are all in flight together; l and O of resumed rows are loaded right
+//     before the first tile and arrive behind its QK products.  The state rows are written
+//     back through LDS, four whole rows per store instruction.
 //   * Workgroups are ordered so that each XCD works on a contiguous set of heads (their K/V
 //     stay in that XCD's L2) and the query tiles that see the most keys start first.
+//   * Up to 64 query rows per (sequence, head) (Mode B, decode-like calls): the split-key form,
+//     where the wavefronts split every tile's keys instead of its rows (see SPLIT below).
 #include <hip/hip_fp16.h>
 
 #include "q8attn_internal.h"
