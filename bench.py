@@ -38,11 +38,39 @@ KERNEL_SOURCES = ["chunked_flashattention_q8_amd/csrc/attn.hip",
                   "chunked_flashattention_q8_amd/csrc/q8attn_internal.h"]
 
 
+def code_tokens(src: str) -> str:
+    """The source with its comments and its whitespace outside string and character literals
+    removed, so that an edit of a comment or of layout leaves it unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif c.isspace():
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash() -> str:
+    """SHA-256 of the accumulate kernel's code (comments and layout excluded): the key under
+    which the committed HBM traffic summary is valid."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()
 
 
