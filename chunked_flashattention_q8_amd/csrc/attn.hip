@@ -331,9 +331,11 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     int kv_end_b[NJ], kv_full_b[NJ], qi[NJ], lim[NJ];
     bool q_ok[NJ];
     int64_t row[NJ];
+    // first query row of this wavefront's j-th block (wavefront-uniform)
+    auto block_q0 = [&](int j) { return q_wg0 + WQ * (SPLIT ? (wave & 1) : (j == 0 ? wave : 7 - wave)); };
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int q0 = q_wg0 + WQ * (SPLIT ? (wave & 1) : (j == 0 ? wave : 7 - wave));
+        const int q0 = block_q0(j);
         const bool live = q0 < a.M;
         kv_end_b[j] = live ? kv_end_for(min(q0 + WQ, a.M) - 1) : 0;
         kv_full_b[j] = (q0 + WQ <= a.M) ? kv_end_for(q0) : 0;
@@ -399,13 +401,14 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     };
 
     // Loads past the chunk read as zero, and operand tiles unpacked from raw rows past the last
-    // tile are never read, so fetch and unpack run unconditionally (no branches inside the
-    // tile loop's scheduling regions).
+    // tile are never read, so unpack runs unconditionally (no branches inside the tile loop's
+    // scheduling regions); copies are skipped past the last tile.
     // Prologue: the first two tiles' copies, then every row's Q and m, all in flight together;
     // the resumed rows' l and O are loaded after it, their latency covered by the first tile's
     // QK work (they are first used by its rescale or PV products).
     fetch(0, 0);
-    fetch(1, 1);
+    if (n_tiles > 1)
+        fetch(1, 1);
 
     half8 qreg[NJ][4];
     floatx16 o[NJ][2];
@@ -455,6 +458,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(a.o + head * a.M * kHeadDim,
                                                   (uint32_t)a.M * kHeadDim * 4u);
     const __amdgpu_buffer_rsrc_t rs_l = make_rsrc(a.l + head * a.M, (uint32_t)a.M * 4u);
+    const __amdgpu_buffer_rsrc_t rs_m = make_rsrc(a.m + head * a.M, (uint32_t)a.M * 4u);
     // past-the-end offset: beyond the largest range (n_q < 2^24 rows of 256 bytes, checked on
     // the host) even with the 240 bytes a row's last piece adds, and without wrapping
     constexpr uint32_t kNoRow = 0xFFFFFF00u;
@@ -479,7 +483,10 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     };
 
     auto tile = [&](const int t) {
-        fetch(t + 2, t & 1); // raw buffer t&1 was unpacked in the previous interval
+        // raw buffer t&1 was unpacked in the previous interval; no copies past the last tile
+        // (for a workgroup on the causal diagonal they would be real reads)
+        if (t + 2 < n_tiles)
+            fetch(t + 2, t & 1);
         const KvTile<FMT> &T = sm.tile[t & 1];
         const int key0 = t * KT;
         // tile t+1 is unpacked from its raw rows in every branch: the same barrier interval
@@ -729,22 +736,28 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     make_float4(o[j][1][4 * k] * rr, o[j][1][4 * k + 1] * rr,
                                 o[j][1][4 * k + 2] * rr, o[j][1][4 * k + 3] * rr);
             }
-            if (g == 0) {
+            // rows that are not written address past the head's range, where buffer stores
+            // are dropped
+            const uint32_t q0 = (uint32_t)block_q0(j);
+            if (g == 0)
                 stg[WQ * kStagePitch + qcol] = wr ? 1.f : 0.f;
-                if (wr) {
-                    a.m[row[j]] = m_top[j] * kLn2;
-                    a.l[row[j]] = l_tot * rr;
-                }
-            }
-            // the same wavefront reads back what it wrote (LDS keeps a wavefront's order)
-            float4 *oblk = reinterpret_cast<float4 *>(a.o + (row[j] - qcol) * kHeadDim);
+            const uint32_t ml_off = (wr && g == 0) ? (q0 + qcol) * 4u : kNoRow;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_top[j] * kLn2), rs_m, ml_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot * rr), rs_l, ml_off, 0, 0);
+            // the same wavefront reads back what it wrote (LDS keeps a wavefront's order): all
+            // rows and flags first, so the LDS reads overlap, then the stores
+            u32x4 vv[WQ / 4];
+            uint32_t off[WQ / 4];
 #pragma unroll
             for (int i = 0; i < WQ / 4; ++i) {
                 const int r = 4 * i + (lane >> 4), c = lane & 15;
-                const float4 v = *reinterpret_cast<const float4 *>(&stg[r * kStagePitch + 4 * c]);
-                if (stg[WQ * kStagePitch + r] != 0.f)
-                    oblk[r * (kHeadDim / 4) + c] = v;
+                vv[i] = *reinterpret_cast<const u32x4 *>(&stg[r * kStagePitch + 4 * c]);
+                off[i] = stg[WQ * kStagePitch + r] != 0.f
+                             ? (q0 + r) * (kHeadDim * 4u) + 16u * c : kNoRow;
             }
+#pragma unroll
+            for (int i = 0; i < WQ / 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(vv[i], rs_o, off[i], 0, 0);
         }
     }
 }
