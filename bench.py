@@ -94,7 +94,9 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
 
 
-def run_resident(w, kv_dtype, chunk, steps, warmup):
+def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True):
+    """Time the resident step of workload w; inputs = (q, k, v) already drawn for w, or None.
+    graph=False skips the captured-graph pass and the append measurement."""
     import numpy as np
     import torch
 
@@ -102,8 +104,11 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
     import synthetic
 
     dev = torch.device("cuda:0")
-    q = synthetic.gen_q(w)
-    k, v = synthetic.gen_kv(w)
+    if inputs is None:
+        q = synthetic.gen_q(w)
+        k, v = synthetic.gen_kv(w)
+    else:
+        q, k, v = inputs
     qd = torch.from_numpy(q).view(torch.float16).to(dev)
     if kv_dtype == q8a.KV_Q8_0:
         kx = torch.from_numpy(k).to(dev)
@@ -177,6 +182,14 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
         if pairs:
             d = [a.elapsed_time(b) for a, b in pairs]
             kern[key] = {"launches_per_step": len(d) // steps, "mean_us": 1e3 * float(np.mean(d))}
+    acc_ms = [a.elapsed_time(b) for a, b in ev["accumulate"]]
+    res = dict(q=q, out=out, lse=lse, ms_clean=ms_clean, ms_events=ms_events, kernels=kern,
+               acc_mean_ms=float(np.mean(acc_ms)), acc_flops_mean=float(np.mean(acc_flops)),
+               acc_per_chunk_us=[1e3 * float(np.mean(acc_ms[i::len(chunks)]))
+                                 for i in range(len(chunks))],
+               acc_flops=acc_flops, k=k, v=v, chunks=chunks, append=None)
+    if not graph:
+        return res
     # the same step captured once into a HIP graph and replayed: a secondary, labelled number
     # (fewer launch gaps); every replay must reproduce the eager output bit for bit
     ref_out, ref_lse = out.clone(), lse.clone()
@@ -195,18 +208,9 @@ def run_resident(w, kv_dtype, chunk, steps, warmup):
     torch.cuda.synchronize()
     ms_graph = t0.elapsed_time(t1) / steps
     graph_equal = graph_equal and bool(torch.equal(out, ref_out) and torch.equal(lse, ref_lse))
-    append = None
+    res["ms_graph"], res["graph_equal"] = ms_graph, graph_equal
     if (kv_dtype == q8a.KV_Q8_0 and w.q_pos0 > 0 and chunks[-1][0] == w.q_pos0 and w.B == 1):
-        append = measure_append(w, qd, kx, vx, kd, vd, m, l, o, out, lse, chunks, steps)
-    acc_ms = [a.elapsed_time(b) for a, b in ev["accumulate"]]
-    acc_mean_ms = float(np.mean(acc_ms))
-    acc_flops_mean = float(np.mean(acc_flops))
-    res = dict(q=q, out=out, lse=lse, ms_clean=ms_clean, ms_events=ms_events, kernels=kern,
-               ms_graph=ms_graph, graph_equal=graph_equal,
-               acc_mean_ms=acc_mean_ms, acc_flops_mean=acc_flops_mean,
-               acc_per_chunk_us=[1e3 * float(np.mean(acc_ms[i::len(chunks)]))
-                                 for i in range(len(chunks))],
-               acc_flops=acc_flops, k=k, v=v, chunks=chunks, append=append)
+        res["append"] = measure_append(w, qd, kx, vx, kd, vd, m, l, o, out, lse, chunks, steps)
     return res
 
 
@@ -583,6 +587,37 @@ def streamed_line(w, args):
     print(json.dumps(line), flush=True)
 
 
+def secondary_points(main_w, main_res, steps, warmup):
+    """The other resident points of the graded shape, each timed like the main step (labelled
+    secondary numbers, not the line's value): the single-sequence M=2048 prefill, the same 8
+    sequences with FP16 KV (the same draws rounded to FP16, which isolates the dequantisation
+    cost) and with the whole KV sequence in one chunk call (B_C = 2048, no state round trips)."""
+    import chunked_flashattention_q8_amd as q8a
+    import synthetic
+
+    out = {}
+    same = (main_res["q"], main_res["k"], main_res["v"])
+    points = [("incore_m2048_q8_0_bc512", synthetic.WORKLOADS[1], q8a.KV_Q8_0, 512, None),
+              ("batch8_m2048_f16kv_bc512", main_w, q8a.KV_F16, 512, same),
+              ("batch8_m2048_q8_0_bc2048", main_w, q8a.KV_Q8_0, 2048, same)]
+    for name, w, kv, chunk, inputs in points:
+        r = run_resident(w, kv, chunk, steps, warmup, inputs=inputs, graph=False)
+        flops = w.visible_pairs() * 4 * w.D
+        acc = r["acc_flops_mean"] / (r["acc_mean_ms"] * 1e-3) / 1e12
+        out[name] = {
+            "ms_per_step": round(r["ms_clean"], 5),
+            "value": round(flops / (r["ms_clean"] * 1e-3) / 1e12, 3),
+            "step_fraction_of_mfma_peak": round(flops / (r["ms_clean"] * 1e-3) / 1e12 /
+                                                PEAK_F16_TFLOPS, 4),
+            "accumulate_mean_launch_us": round(1e3 * r["acc_mean_ms"], 3),
+            "accumulate_frac": round(acc / PEAK_F16_TFLOPS, 4),
+            "chunk_calls": len(r["chunks"]),
+            "step": "pack K,V + init + chunk calls + finalize" if kv == q8a.KV_Q8_0
+                    else "init + chunk calls + finalize (FP16 KV needs no pack)",
+        }
+    return out
+
+
 def cpu_baseline(w, res, kv_dtype, budget_s):
     """The oracle on whole heads (b, h) in order until ~budget_s of wall time has passed."""
     import numpy as np
@@ -742,6 +777,9 @@ def main():
     ap.add_argument("--kv", choices=["q8_0", "f16"], default="q8_0")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary points of the default line (single sequence, "
+                         "FP16 KV, B_C = 2048)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-summary", nargs=5,
                     metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "MIB"),
@@ -832,6 +870,8 @@ def main():
     }
     if res["append"]:
         line["append"] = res["append"]
+    if args.workload == 2 and args.chunk is None and args.kv == "q8_0" and not args.no_secondary:
+        line["secondary"] = secondary_points(w, res, min(args.steps, 20), min(args.warmup, 3))
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, res, kv_dtype, args.cpu_seconds)
         line["cpu_baseline"] = base
