@@ -94,9 +94,12 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
 
 
-def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True):
+def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, fused=True):
     """Time the resident step of workload w; inputs = (q, k, v) already drawn for w, or None.
-    graph=False skips the captured-graph pass and the append measurement."""
+    graph=False skips the captured-graph pass and the append measurement.  fused: the chunk
+    calls write the final output of the rows each completes (attn_accumulate_chunk_final), and
+    attn_finalize runs only if some rows are left (queries past the end of the cache);
+    otherwise plain chunk calls and a finalize launch."""
     import numpy as np
     import torch
 
@@ -150,11 +153,18 @@ def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True):
         timed("init", init, record)
         kp, vp = kd.data_ptr(), vd.data_ptr()
         for s, n in chunks:
-            timed("accumulate",
-                  lambda s=s, n=n: q8a.attn_accumulate_chunk(
-                      st[0], qd, kp + s * row, vp + s * row, kv_dtype, s, n, w.N * row,
-                      w.H * w.N * row, 1), record)
-        timed("finalize", lambda: q8a.attn_finalize(st[0], out, lse), record)
+            if fused:
+                timed("accumulate",
+                      lambda s=s, n=n: q8a.attn_accumulate_chunk_final(
+                          st[0], qd, kp + s * row, vp + s * row, kv_dtype, s, n, w.N * row,
+                          w.H * w.N * row, out, lse), record)
+            else:
+                timed("accumulate",
+                      lambda s=s, n=n: q8a.attn_accumulate_chunk(
+                          st[0], qd, kp + s * row, vp + s * row, kv_dtype, s, n, w.N * row,
+                          w.H * w.N * row, 1), record)
+        if not fused or w.q_pos0 + w.M > w.N:
+            timed("finalize", lambda: q8a.attn_finalize(st[0], out, lse), record)
 
     for _ in range(warmup):
         step(False)
@@ -589,19 +599,21 @@ def streamed_line(w, args):
 
 def secondary_points(main_w, main_res, steps, warmup):
     """The other resident points of the graded shape, each timed like the main step (labelled
-    secondary numbers, not the line's value): the single-sequence M=2048 prefill, the same 8
-    sequences with FP16 KV (the same draws rounded to FP16, which isolates the dequantisation
-    cost) and with the whole KV sequence in one chunk call (B_C = 2048, no state round trips)."""
+    secondary numbers, not the line's value): the same step with plain chunk calls and a
+    separate finalize launch, the single-sequence M=2048 prefill, the same 8 sequences with FP16
+    KV (the same draws rounded to FP16, which isolates the dequantisation cost) and with the
+    whole KV sequence in one chunk call (B_C = 2048, no state round trips)."""
     import chunked_flashattention_q8_amd as q8a
     import synthetic
 
     out = {}
     same = (main_res["q"], main_res["k"], main_res["v"])
-    points = [("incore_m2048_q8_0_bc512", synthetic.WORKLOADS[1], q8a.KV_Q8_0, 512, None),
-              ("batch8_m2048_f16kv_bc512", main_w, q8a.KV_F16, 512, same),
-              ("batch8_m2048_q8_0_bc2048", main_w, q8a.KV_Q8_0, 2048, same)]
-    for name, w, kv, chunk, inputs in points:
-        r = run_resident(w, kv, chunk, steps, warmup, inputs=inputs, graph=False)
+    points = [("batch8_m2048_q8_0_bc512_finalize_launch", main_w, q8a.KV_Q8_0, 512, same, False),
+              ("incore_m2048_q8_0_bc512", synthetic.WORKLOADS[1], q8a.KV_Q8_0, 512, None, True),
+              ("batch8_m2048_f16kv_bc512", main_w, q8a.KV_F16, 512, same, True),
+              ("batch8_m2048_q8_0_bc2048", main_w, q8a.KV_Q8_0, 2048, same, True)]
+    for name, w, kv, chunk, inputs, fused in points:
+        r = run_resident(w, kv, chunk, steps, warmup, inputs=inputs, graph=False, fused=fused)
         flops = w.visible_pairs() * 4 * w.D
         acc = r["acc_flops_mean"] / (r["acc_mean_ms"] * 1e-3) / 1e12
         out[name] = {
@@ -612,8 +624,9 @@ def secondary_points(main_w, main_res, steps, warmup):
             "accumulate_mean_launch_us": round(1e3 * r["acc_mean_ms"], 3),
             "accumulate_frac": round(acc / PEAK_F16_TFLOPS, 4),
             "chunk_calls": len(r["chunks"]),
-            "step": "pack K,V + init + chunk calls + finalize" if kv == q8a.KV_Q8_0
-                    else "init + chunk calls + finalize (FP16 KV needs no pack)",
+            "step": ("pack K,V + " if kv == q8a.KV_Q8_0 else "(FP16 KV: no pack) ") +
+                    ("init + chunk calls writing the final rows" if fused else
+                     "init + plain chunk calls + a finalize launch"),
         }
     return out
 
@@ -692,10 +705,11 @@ def traffic_per_launch():
     return float(t["hbm_bytes_per_launch"])
 
 
-def algorithmic_bytes(w, chunk):
+def algorithmic_bytes(w, chunk, fused=True):
     """Algorithmic HBM bytes of each chunk call: the chunk's K and V rows (136 B per key per
     head), Q rows of the queries that see the chunk (128 B), their state read (m; l and O only
-    for rows that are not empty) and written (m, l, O: 264 B)."""
+    for rows that are not empty) and written (m, l, O: 264 B); fused, also the final output of
+    the rows whose position lies in the chunk (FP16 out 128 B, lse 4 B)."""
     import numpy as np
     pos = w.q_pos0 + np.arange(w.M, dtype=np.int64)
     out = []
@@ -703,7 +717,8 @@ def algorithmic_bytes(w, chunk):
         n = min(chunk, w.N - s)
         touched = int((pos >= s).sum())
         nonempty = int((pos >= s).sum()) if s > 0 else 0  # every row sees key 0 first
-        per_head = n * 136 + touched * (128 + 4 + 264) + nonempty * 260
+        final = int(((pos >= s) & (pos < s + n)).sum()) if fused else 0
+        per_head = n * 136 + touched * (128 + 4 + 264) + nonempty * 260 + final * 132
         out.append(per_head * w.B * w.H)
     return out
 
@@ -841,7 +856,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "%s: B=%d H=%d M=%d N=%d d=64 causal q_pos0=%d, %s KV, B_C=%d "
-                        "(%d chunk calls); step = pack K,V + init + chunk calls + finalize"
+                        "(%d chunk calls); step = pack K,V + init + chunk calls, each writing "
+                        "the final out/lse of the rows it completes"
                         % (w.name, w.B, w.H, w.M, w.N, w.q_pos0, args.kv.upper(), chunk,
                            len(res["chunks"])),
             "kv_dtype": args.kv, "chunk_tokens": chunk,

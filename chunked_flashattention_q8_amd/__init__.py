@@ -35,7 +35,8 @@ STATE_MAGIC = 0x51384154
 HEAD_DIM = 64
 ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
 
-EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_append_chunk",
+EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk",
+           "attn_accumulate_chunk_final", "attn_append_chunk",
            "attn_finalize",
            "attn_state_merge", "attn_accumulate_stream", "attn_accumulate_file",
            "q8a_status_string",
@@ -78,6 +79,8 @@ def library() -> ctypes.CDLL:
     lib.q8_0_pack.argtypes = [P, P, i64, i32, P]
     lib.attn_state_init.argtypes = [SP, P, P, P, i32, i32, i32, i32, i64, P]
     lib.attn_accumulate_chunk.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P]
+    lib.attn_accumulate_chunk_final.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P,
+                                                P, P]
     lib.attn_append_chunk.argtypes = [SP, P, P, P, P, P, i64, i32, i64, i64, i32, P]
     lib.attn_finalize.argtypes = [SP, P, P, P]
     lib.attn_state_merge.argtypes = [SP, SP, P]
@@ -148,6 +151,18 @@ def attn_accumulate_chunk(st: q8a_state, q, k, v, kv_dtype: int, kv_pos0: int, n
                                            int(kv_dtype), int(kv_pos0), int(n_kv),
                                            int(kv_head_stride), int(kv_seq_stride),
                                            int(causal), _stream(stream)))
+
+
+def attn_accumulate_chunk_final(st: q8a_state, q, k, v, kv_dtype: int, kv_pos0: int, n_kv: int,
+                                kv_head_stride: int, kv_seq_stride: int, out, lse=None,
+                                causal: int = 1, stream=None) -> None:
+    """attn_accumulate_chunk, plus out/lse of the rows whose query position lies in the chunk
+    (final in a causal pass over chunks in ascending key order)."""
+    _check(library().attn_accumulate_chunk_final(ctypes.byref(st), _ptr(q), _ptr(k), _ptr(v),
+                                                 int(kv_dtype), int(kv_pos0), int(n_kv),
+                                                 int(kv_head_stride), int(kv_seq_stride),
+                                                 int(causal), _ptr(out), _ptr(lse),
+                                                 _stream(stream)))
 
 
 def attn_append_chunk(st: q8a_state, q, k_new, v_new, k_cache, v_cache, kv_pos0: int, n_kv: int,

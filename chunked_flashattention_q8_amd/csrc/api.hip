@@ -98,6 +98,8 @@ q8a::AccumulateArgs make_args(const q8a_state *st, const void *q, const void *k,
     a.M = st->n_q;
     a.n_kv = n_kv;
     a.causal = causal;
+    a.out = nullptr;
+    a.lse = nullptr;
     return a;
 }
 
@@ -183,6 +185,45 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
         return rc;
     q8a::AccumulateArgs a =
         make_args(st, q, k, v, kv_pos0, n_kv, kv_head_stride, kv_seq_stride, causal);
+    hipError_t e = q8a::launch_accumulate(a, kv_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8A_OK : hip_failure(e);
+}
+
+int attn_accumulate_chunk_final(const q8a_state *st, const void *q, const void *k,
+                                const void *v, int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
+                                int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
+                                void *out, float *lse, void *stream)
+{
+    int rc = check_chunk(st, q, k, v, kv_dtype, kv_pos0, n_kv, kv_head_stride, kv_seq_stride,
+                         causal);
+    if (rc)
+        return rc;
+    if (causal != 1 || !out)
+        return Q8A_E_INVAL;
+    if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+        return Q8A_E_ALIGN;
+    // the outputs must not overlap anything the launch reads or writes
+    const int64_t rows = state_rows(st);
+    auto overlap = [](const void *a, int64_t na, const void *b, int64_t nb) {
+        const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+        return x < y + nb && y < x + na;
+    };
+    const int64_t row = kv_dtype == Q8A_KV_Q8_0 ? q8a::kQ8RowBytes : q8a::kF16RowBytes;
+    const int64_t kv_span = (int64_t)(st->n_seq - 1) * kv_seq_stride +
+                            (int64_t)(st->n_heads - 1) * kv_head_stride + (int64_t)n_kv * row;
+    const void *used[6] = {q, k, v, st->m, st->l, st->o};
+    const int64_t spans[6] = {rows * q8a::kHeadDim * 2, kv_span, kv_span, rows * 4, rows * 4,
+                              rows * q8a::kHeadDim * 4};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(out, rows * q8a::kHeadDim * 2, used[i], spans[i]) ||
+            (lse && overlap(lse, rows * 4, used[i], spans[i])))
+            return Q8A_E_INVAL;
+    if (lse && overlap(out, rows * q8a::kHeadDim * 2, lse, rows * 4))
+        return Q8A_E_INVAL;
+    q8a::AccumulateArgs a =
+        make_args(st, q, k, v, kv_pos0, n_kv, kv_head_stride, kv_seq_stride, causal);
+    a.out = out;
+    a.lse = lse;
     hipError_t e = q8a::launch_accumulate(a, kv_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }

@@ -716,17 +716,27 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     // Each wavefront stages its 32-row block in LDS (its own region, past the area the merge
     // above uses) and stores whole rows: 4 contiguous rows (1 KiB) per store instruction, instead
     // of 32-byte pieces of 32 rows.  A row's write flag travels with it.
+    // With a.out set, the rows whose query position lies inside the chunk are final (in a
+    // causal pass over chunks in ascending key order no later key is visible to them): their
+    // out and lse are written as the finalize kernel would from the state just stored (the same
+    // FP32 values, the same division and logarithm), flag 2 instead of 1.
     constexpr int kStagePitch = 68;                                // floats per staged row
-    constexpr int kStageFloats = WQ * kStagePitch + WQ;            // rows, then the flags
+    constexpr int kStageFloats = WQ * kStagePitch + 2 * WQ;        // rows, flags, final l
     constexpr int kStageBase = 2 * 64 * 36;                        // floats
     static_assert(sizeof(Smem<FMT>) >= 4 * (kStageBase + 4 * kStageFloats), "staging area");
     float *stg = reinterpret_cast<float *>(&sm) + kStageBase + wave * kStageFloats;
+    float *stg_flag = stg + WQ * kStagePitch, *stg_l = stg_flag + WQ;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (kv_end_b[j] > 0 && (!SPLIT || kh == 0)) { // uniform per wavefront
             const float l_tot = half_swap_sum(l_part[j]);
             const bool wr = q_ok[j] && saw[j];
             const float rr = wr ? __builtin_amdgcn_exp2f(m_ref[j] - m_top[j]) : 0.f;
+            const int64_t pos = a.q_pos0 + qi[j]; // this lane's query position
+            const bool fin = a.out && wr && pos >= a.kv_pos0 && pos < a.kv_pos0 + a.n_kv;
+            // does the block hold a final row (wavefront-uniform)?
+            const int64_t p0 = a.q_pos0 + block_q0(j);
+            const bool fin_block = a.out && p0 + WQ > a.kv_pos0 && p0 < a.kv_pos0 + a.n_kv;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 *reinterpret_cast<float4 *>(&stg[qcol * kStagePitch + 8 * k + 4 * g]) =
@@ -739,11 +749,19 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             // rows that are not written address past the head's range, where buffer stores
             // are dropped
             const uint32_t q0 = (uint32_t)block_q0(j);
-            if (g == 0)
-                stg[WQ * kStagePitch + qcol] = wr ? 1.f : 0.f;
+            const float m_st = m_top[j] * kLn2, l_st = l_tot * rr; // the stored m and l
+            if (g == 0) {
+                stg_flag[qcol] = wr ? (fin ? 2.f : 1.f) : 0.f;
+                stg_l[qcol] = l_st;
+            }
             const uint32_t ml_off = (wr && g == 0) ? (q0 + qcol) * 4u : kNoRow;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_top[j] * kLn2), rs_m, ml_off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot * rr), rs_l, ml_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_st), rs_m, ml_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_st), rs_l, ml_off, 0, 0);
+            if (fin_block && a.lse)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(m_st + logf(l_st)),
+                    make_rsrc(a.lse + head * a.M, (uint32_t)a.M * 4u),
+                    (fin && g == 0) ? (q0 + qcol) * 4u : kNoRow, 0, 0);
             // the same wavefront reads back what it wrote (LDS keeps a wavefront's order): all
             // rows and flags first, so the LDS reads overlap, then the stores
             u32x4 vv[WQ / 4];
@@ -752,12 +770,30 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             for (int i = 0; i < WQ / 4; ++i) {
                 const int r = 4 * i + (lane >> 4), c = lane & 15;
                 vv[i] = *reinterpret_cast<const u32x4 *>(&stg[r * kStagePitch + 4 * c]);
-                off[i] = stg[WQ * kStagePitch + r] != 0.f
-                             ? (q0 + r) * (kHeadDim * 4u) + 16u * c : kNoRow;
+                off[i] = stg_flag[r] != 0.f ? (q0 + r) * (kHeadDim * 4u) + 16u * c : kNoRow;
             }
 #pragma unroll
             for (int i = 0; i < WQ / 4; ++i)
                 __builtin_amdgcn_raw_buffer_store_b128(vv[i], rs_o, off[i], 0, 0);
+            if (fin_block) {
+                // out = O / l rounded once to FP16, 4 values per lane and row
+                const __amdgpu_buffer_rsrc_t rs_out =
+                    make_rsrc(reinterpret_cast<_Float16 *>(a.out) + head * a.M * kHeadDim,
+                              (uint32_t)a.M * (kHeadDim * 2u));
+#pragma unroll
+                for (int i = 0; i < WQ / 4; ++i) {
+                    const int r = 4 * i + (lane >> 4), c = lane & 15;
+                    const float lv = stg_l[r];
+                    const uint32_t oo =
+                        stg_flag[r] == 2.f ? (q0 + r) * (kHeadDim * 2u) + 8u * c : kNoRow;
+                    const half4 h = {(_Float16)(__uint_as_float(vv[i][0]) / lv),
+                                     (_Float16)(__uint_as_float(vv[i][1]) / lv),
+                                     (_Float16)(__uint_as_float(vv[i][2]) / lv),
+                                     (_Float16)(__uint_as_float(vv[i][3]) / lv)};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rs_out,
+                                                          oo, 0, 0);
+                }
+            }
         }
     }
 }

@@ -24,6 +24,10 @@ struct AccumulateArgs {
     int32_t B, H, M;
     int32_t n_kv;
     int32_t causal;
+    // optional: the final output of the rows whose query position lies inside the chunk
+    // (null: none); out FP16 [B][H][M][64], lse FP32 [B][H][M] or null
+    void *out;
+    float *lse;
 };
 
 hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s);

@@ -114,6 +114,25 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
                           int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
                           void *stream);
 
+/* attn_accumulate_chunk, and in the same launch the final output of the rows this chunk
+ * completes ("Out-of-Core ...", Sec. 3: the final normalisation O / l and m + ln l, applied as
+ * soon as a row has seen its last key).  With causal masking and the chunks of a pass given in
+ * ascending key order, a row whose query position p lies inside the chunk (kv_pos0 <= p <
+ * kv_pos0 + n_kv) sees no key of any later chunk: its out and lse are written as attn_finalize
+ * would write them from the state after this call, bit for bit.  Other rows' out and lse are
+ * not touched, and the state is updated exactly as by attn_accumulate_chunk (so attn_finalize
+ * still works afterwards).  The caller guarantees the order: every key before kv_pos0 that such
+ * a row sees must already be in the state.
+ *   causal   must be 1 (Q8A_E_INVAL otherwise).
+ *   out      FP16 [n_seq][n_heads][n_q][64], 16-byte aligned;  lse  FP32 [..][n_q], 4-byte
+ *            aligned, or NULL.  Neither may overlap Q, K, V, the state or each other
+ *            (Q8A_E_INVAL).
+ * Everything else as for attn_accumulate_chunk. */
+int attn_accumulate_chunk_final(const q8a_state *st, const void *q, const void *k,
+                                const void *v, int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
+                                int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
+                                void *out, float *lse, void *stream);
+
 /* Quantise-on-append: pack n_kv newly appended tokens of K and V into the Q8_0 cache and
  * accumulate them into the state, in one call.  The cache entries are quantised dynamically as
  * they arrive ("Core Architecture & The 4-Brick Pipeline", Sec. 5: dynamically quantised

@@ -173,6 +173,42 @@ def test_append_valid_layouts_pass_validation():
     assert append(st2, hs=2 * 64 * 68, ss=64 * 68) == q8a.Q8A_E_HIP
 
 
+def acc_final(st, q=0x3000000, k=0x4000000, v=0x5000000, out=0x1000000, lse=0x2000000,
+              pos=0, n=64, causal=1):
+    P = ctypes.c_void_p
+    return q8a.library().attn_accumulate_chunk_final(
+        ctypes.byref(st), P(q), P(k), P(v), 0, pos, n, 256 * 68, 0, causal, P(out),
+        P(lse) if lse else None, None)
+
+
+def separate_state():
+    st = fake_state()
+    st.m, st.l, st.o = 0x6000000, 0x7000000, 0x8000000
+    return st
+
+
+def test_accumulate_final_rejects_bad_arguments():
+    st = separate_state()
+    assert acc_final(q8a.q8a_state()) == q8a.Q8A_E_STATE       # not initialised
+    assert acc_final(st, n=0) == q8a.Q8A_E_INVAL                # the chunk checks apply
+    assert acc_final(st, causal=0) == q8a.Q8A_E_INVAL           # final rows need the causal mask
+    assert acc_final(st, out=0) == q8a.Q8A_E_INVAL
+    assert acc_final(st, out=0x1000000 + 8) == q8a.Q8A_E_ALIGN
+    assert acc_final(st, lse=0x2000000 + 2) == q8a.Q8A_E_ALIGN
+    assert acc_final(st, out=0x3000000 + 4096) == q8a.Q8A_E_INVAL   # out over Q
+    assert acc_final(st, out=0x8000000) == q8a.Q8A_E_INVAL          # out over the state's O
+    assert acc_final(st, lse=0x6000000) == q8a.Q8A_E_INVAL          # lse over the state's m
+    assert acc_final(st, lse=0x1000000 + 1024) == q8a.Q8A_E_INVAL   # lse over out
+    assert acc_final(st, out=0x4000000 - 64) == q8a.Q8A_E_INVAL     # out runs into K
+
+
+@pytest.mark.skipif(not NO_GPU, reason="needs a host without a GPU")
+def test_accumulate_final_valid_arguments_pass_validation():
+    st = separate_state()
+    assert acc_final(st) == q8a.Q8A_E_HIP
+    assert acc_final(st, lse=0) == q8a.Q8A_E_HIP
+
+
 def test_finalize_rejects_bad_arguments():
     lib = q8a.library()
     P = ctypes.c_void_p

@@ -1,0 +1,89 @@
+"""attn_accumulate_chunk_final: a causal chunk call that also writes the final output of the rows
+whose query position lies inside the chunk.  Against the plain path (attn_accumulate_chunk for
+every chunk, then attn_finalize) on the same inputs: the state after the pass is the same bit for
+bit, out and lse of every row some chunk completes are the same bit for bit, and the rows no
+chunk completes keep what out and lse held before.  The completed rows also meet the oracle at
+the output tolerances.  Cases cover both tile forms (more and at most 64 query rows), FP16 KV,
+partial last chunks, queries past the end of the cache and chunks that no query sees."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_flashattention_q8_amd as q8a
+from gpu_util import D, assert_close, dev, prefill, say
+from test_gpu_attn import chunk_list, setup_case
+
+pytestmark = pytest.mark.gpu
+
+Q8, F16 = q8a.KV_Q8_0, q8a.KV_F16
+
+CASES = [
+    # B, H, M, N, q_pos0, chunk, kv dtype; the chunks cover keys [0, N) (N a multiple of 4)
+    (1, 2, 200, 200, 0, 64, Q8),      # every row completed in its diagonal chunk, ragged tiles
+    (2, 3, 132, 336, 204, 100, Q8),   # rows completed by the last two chunks, partial last chunk
+    (1, 2, 31, 96, 65, 12, Q8),       # at most 64 rows (split-key form), many small chunks
+    (2, 2, 33, 292, 259, 64, Q8),     # split-key form, the second block holds one row
+    (1, 2, 300, 600, 100, 128, Q8),   # chunks past the last query position touch no row
+    (1, 2, 100, 60, 0, 32, Q8),       # rows at positions 60..99 are never completed
+    (2, 2, 200, 200, 0, 64, F16),     # FP16 KV
+    (1, 3, 520, 520, 0, 520, Q8),     # one chunk completes every row
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_final_rows_match_finalize(orc, case):
+    B, H, M, N, q_pos0, bc, kv = case
+    say("case", case)
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=sum(case[:6]), kv_dtype=kv)
+    chunks = chunk_list(N, bc)
+    out_ref, lse_ref, (m1, l1, o1) = prefill(qd, kd, vd, kv, B, H, M, N, q_pos0, chunks)
+
+    row = q8a.ROW_BYTES[kv]
+    m, l, o = q8a.alloc_state(B, H, M)
+    st = q8a.attn_state_init(m, l, o, B, H, M, D, q_pos0)
+    # sentinels: the rows no chunk completes must keep them
+    out = torch.full((B, H, M, D), 7.0, dtype=torch.float16, device=dev())
+    lse = torch.full((B, H, M), -3.0, dtype=torch.float32, device=dev())
+    kp, vp = kd.data_ptr(), vd.data_ptr()
+    for s, n in chunks:
+        q8a.attn_accumulate_chunk_final(st, qd, kp + s * row, vp + s * row, kv, s, n, N * row,
+                                        H * N * row, out, lse)
+    torch.cuda.synchronize()
+
+    # the state: as the plain chunk calls left it (O of rows that stayed empty is never written)
+    mg, lg = m.cpu().numpy().reshape(-1), l.cpu().numpy().reshape(-1)
+    assert np.array_equal(mg.view(np.uint32), m1.cpu().numpy().reshape(-1).view(np.uint32))
+    assert np.array_equal(lg.view(np.uint32), l1.cpu().numpy().reshape(-1).view(np.uint32))
+    ne = ~np.isneginf(mg)
+    assert np.array_equal(o.cpu().numpy().reshape(-1, D)[ne].view(np.uint32),
+                          o1.cpu().numpy().reshape(-1, D)[ne].view(np.uint32))
+
+    pos = q_pos0 + np.arange(M)
+    done = np.tile(pos < N, B * H)  # completed by the chunk holding its position
+    og = out.cpu().numpy().reshape(-1, D)
+    lg2 = lse.cpu().numpy().reshape(-1)
+    orf = out_ref.cpu().numpy().reshape(-1, D)
+    lrf = lse_ref.cpu().numpy().reshape(-1)
+    assert np.array_equal(og[done].view(np.uint16), orf[done].view(np.uint16))
+    assert np.array_equal(lg2[done].view(np.uint32), lrf[done].view(np.uint32))
+    assert np.all(og[~done] == np.float16(7.0)) and np.all(lg2[~done] == np.float32(-3.0))
+
+    O_ref, lse_o = orc.attention(prob)
+    if done.any():
+        assert_close(og[done].astype(np.float32), lg2[done], O_ref[done], lse_o[done],
+                     "completed rows " + str(case))
+
+
+def test_final_without_lse(orc):
+    """lse may be NULL: out alone is written, the same as with it."""
+    B, H, M, N, q_pos0, bc = 1, 2, 130, 260, 0, 100
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=321)
+    out_ref, _, _ = prefill(qd, kd, vd, Q8, B, H, M, N, q_pos0, chunk_list(N, bc))
+    m, l, o = q8a.alloc_state(B, H, M)
+    st = q8a.attn_state_init(m, l, o, B, H, M, D, q_pos0)
+    out = torch.zeros((B, H, M, D), dtype=torch.float16, device=dev())
+    for s, n in chunk_list(N, bc):
+        q8a.attn_accumulate_chunk_final(st, qd, kd.data_ptr() + s * 68, vd.data_ptr() + s * 68,
+                                        Q8, s, n, N * 68, H * N * 68, out, None)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16))
