@@ -753,7 +753,8 @@ def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mib,
     alg = algorithmic_bytes(w, w.chunk)
     lines = [
         "# HBM traffic of accumulate_kernel<0, false> (Q8_0 KV, the prefill form) per launch, batch8_m2048 workload:",
-        "# 8 sequences x 32 heads, M = N = 2048 causal, d = 64, B_C = 512 (4 launches per step).",
+        "# 8 sequences x 32 heads, M = N = 2048 causal, d = 64, B_C = 512 (4 launches per step,",
+        "# each also writing out and lse of the rows whose position lies in its chunk).",
         "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, averaged over the accumulate dispatches;",
         "# each is scaled by (bytes copied) / (counter x 1024) of a plain device copy of",
         "# %d MiB (torch copy kernel), measured the same way." % cal_mib,
@@ -803,9 +804,9 @@ def main():
     if args.traffic_summary:
         fd, wd, cfd, cwd, mib = args.traffic_summary
         cmds = ["rocprofv3 --pmc FETCH_SIZE -d %s -o f --output-format csv -- "
-                "python bench.py --no-cpu-baseline --steps 3 --warmup 1" % fd,
+                "python bench.py --no-cpu-baseline --no-secondary --steps 3 --warmup 1" % fd,
                 "rocprofv3 --pmc WRITE_SIZE -d %s -o w --output-format csv -- "
-                "python bench.py --no-cpu-baseline --steps 3 --warmup 1" % wd,
+                "python bench.py --no-cpu-baseline --no-secondary --steps 3 --warmup 1" % wd,
                 "rocprofv3 --pmc FETCH_SIZE -d %s -o cf --output-format csv -- "
                 "python bench.py --copy-calibration %s" % (cfd, mib),
                 "rocprofv3 --pmc WRITE_SIZE -d %s -o cw --output-format csv -- "
