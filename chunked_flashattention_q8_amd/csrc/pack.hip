@@ -11,7 +11,8 @@
 // Arithmetic (bit-exact with the CPU oracle): d = amax / 127 with a correctly rounded FP32
 // division; d16 = FP16(d), round to nearest even; q = round(x / d16) with a correctly rounded
 // FP32 division and halves away from zero, clamped to [-127, 127]; an all-zero block gives
-// d16 = 0 and q = 0.
+// d16 = 0 and q = 0.  The quotients are formed by multiplying with the reciprocal of d16 and
+// fall back to the division where that could round differently (see quantise).
 #include <hip/hip_fp16.h>
 
 #include "q8attn_internal.h"
@@ -19,13 +20,28 @@
 namespace q8a {
 namespace {
 
-__device__ __forceinline__ int quantise(float x, float dh)
+// round(x / dh), halves away from zero, clamped to [-127, 127], with x / dh the correctly
+// rounded FP32 quotient z'.  rdh is the hardware reciprocal of dh (relative error at most 2^-23):
+// y = fl(x * rdh) differs from the exact quotient z by at most (2^-23 + 2^-24 + 2^-47) |z|, and z'
+// from z by at most 2^-24 |z|.  With dh = FP16(amax / 127) (zero excepted) |z| < 256, so y and z'
+// differ by less than 2^-14 and round to the same integer unless y lies within 2^-14 of a
+// half-integer.  Such values (|frac(|y|) - 1/2| <= 2^-13: twice the bound, about 1 in 4000) and
+// any |y| >= 255 take the correctly rounded division instead.
+__device__ __forceinline__ int quantise(float x, float dh, float rdh)
 {
     if (dh == 0.0f)
         return 0;
-    float r = roundf(__fdiv_rn(x, dh));
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
+    float y = x * rdh;
+    float ay = fabsf(y);
+    float ti = truncf(ay), fr = ay - ti; // exact for ay < 2^23
+    if (fabsf(fr - 0.5f) <= 0x1p-13f || ay >= 255.0f) {
+        y = __fdiv_rn(x, dh);
+        ay = fabsf(y);
+        ti = truncf(ay);
+        fr = ay - ti;
+    }
+    const float q = fminf(ti + (fr >= 0.5f ? 1.0f : 0.0f), 127.0f);
+    return (int)copysignf(q, y);
 }
 
 // Each lane packs its quarter of U blocks (U x 256 consecutive float4 per workgroup); the U loads
@@ -67,8 +83,9 @@ __global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict
         a = fmaxf(a, __shfl_xor(a, 4, 8));
         const __half d16 = __float2half_rn(__fdiv_rn(a, 127.0f));
         const float dh = __half2float(d16);
-        const int q0 = quantise(v[u].x, dh), q1 = quantise(v[u].y, dh);
-        const int q2 = quantise(v[u].z, dh), q3 = quantise(v[u].w, dh);
+        const float rdh = __builtin_amdgcn_rcpf(dh);
+        const int q0 = quantise(v[u].x, dh, rdh), q1 = quantise(v[u].y, dh, rdh);
+        const int q2 = quantise(v[u].z, dh, rdh), q3 = quantise(v[u].w, dh, rdh);
         if (blk[u] < n_blocks) {
             uint8_t *out = dst + blk[u] * 34;
             if (sub == 0)

@@ -37,6 +37,18 @@ def test_pack_ties_zero_blocks_and_exact_scales(orc):
         k = rng.integers(-126, 126, size=(64, 32)) + 0.5 * (rng.random((64, 32)) < 0.5)
         k[:, 0] = 127
         blocks.append((k * s).astype(np.float32))
+    # values one and two ulps either side of the exact ties: the quotient lands next to a
+    # half-integer, where a product with the reciprocal of the scale may round differently
+    for s in (1.0, 0.0078735352, 3.0):
+        s = float(np.float16(s))
+        k = (rng.integers(-126, 126, size=(64, 32)) + 0.5).astype(np.float32) * np.float32(s)
+        for steps in (1, 2):
+            away = np.where(rng.random(k.shape) < 0.5, np.float32(np.inf), np.float32(-np.inf))
+            x = k.copy()
+            for _ in range(steps):
+                x = np.nextafter(x, away)
+            x[:, 0] = np.float32(127 * s)
+            blocks.append(x.astype(np.float32))
     blocks.append(np.zeros((8, 32), dtype=np.float32))
     tiny = rng.standard_normal((16, 32)).astype(np.float32) * np.float32(1e-3)  # subnormal d16
     blocks.append(tiny)
