@@ -38,6 +38,10 @@
 //     where the wavefronts split every tile's keys instead of its rows (see SPLIT below).
 #include <hip/hip_fp16.h>
 
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
 #include "q8attn_internal.h"
 
 namespace q8a {
@@ -277,11 +281,16 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
 // every tile), with an online-softmax state of its own; the two states of a block are merged
 // through LDS at the end by the rule attn_state_merge uses.  All four wavefronts then work on
 // the 64 rows instead of two of them (each also carrying an empty block).
-template <int FMT, bool SPLIT>
+// NARROW (used when 256-row workgroups would leave compute-unit slots empty, e.g. one sequence
+// of 32 heads): a workgroup takes 128 query rows, wavefront w the 32-row block w over all keys,
+// so twice as many workgroups share the chip; each K/V tile is unpacked for half as many rows.
+template <int FMT, bool SPLIT, bool NARROW>
 __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 {
-    constexpr int NJ = SPLIT ? 1 : 2; // 32-row query blocks per wavefront
-    constexpr int NS = SPLIT ? 1 : 2; // 32-key subtiles per wavefront and tile
+    static_assert(!(SPLIT && NARROW), "one form at a time");
+    constexpr int NJ = (SPLIT || NARROW) ? 1 : 2; // 32-row query blocks per wavefront
+    constexpr int NS = SPLIT ? 1 : 2;             // 32-key subtiles per wavefront and tile
+    constexpr int QTF = NARROW ? QT / 2 : QT;     // query rows per workgroup
     constexpr int ROW = Smem<FMT>::ROW;
     constexpr int RAW16 = KT * ROW / 16;                 // 16-byte pieces per tensor tile
     constexpr int NPRE = FMT == 0 ? 3 : 4;               // prefetch slots per thread
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     // ---- workgroup -> (sequence, head, query tile).  Workgroups are dispatched round-robin over
     // the 8 XCDs; each XCD gets a contiguous set of heads (their K/V stay in its L2) and within
     // it the query tiles that see the most keys come first.
-    const int n_qt = (a.M + QT - 1) / QT;
+    const int n_qt = (a.M + QTF - 1) / QTF;
     const int BH = a.B * a.H;
     const int wg = blockIdx.x;
     int r, head_i;
@@ -320,19 +329,21 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         const int64_t e = a.q_pos0 + qrow - a.kv_pos0 + 1;
         return (int)(e < 0 ? 0 : (e > a.n_kv ? a.n_kv : e));
     };
-    const int q_wg0 = qt * QT;
-    const int kv_end_wg = kv_end_for(min(q_wg0 + QT, a.M) - 1);
+    const int q_wg0 = qt * QTF;
+    const int kv_end_wg = kv_end_for(min(q_wg0 + QTF, a.M) - 1);
     if (kv_end_wg <= 0)
         return; // the whole workgroup sees nothing of this chunk
     const int n_tiles = (kv_end_wg + KT - 1) / KT;
 
     // ---- this wavefront's 32-row query blocks: w and 7 - w of the tile (balances the causal
-    // diagonal across wavefronts); SPLIT: block w & 1
+    // diagonal across wavefronts); SPLIT: block w & 1; NARROW: block w
     int kv_end_b[NJ], kv_full_b[NJ], qi[NJ], lim[NJ];
     bool q_ok[NJ];
     int64_t row[NJ];
     // first query row of this wavefront's j-th block (wavefront-uniform)
-    auto block_q0 = [&](int j) { return q_wg0 + WQ * (SPLIT ? (wave & 1) : (j == 0 ? wave : 7 - wave)); };
+    auto block_q0 = [&](int j) {
+        return q_wg0 + WQ * (SPLIT ? (wave & 1) : NARROW ? wave : (j == 0 ? wave : 7 - wave));
+    };
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int q0 = block_q0(j);
@@ -897,22 +908,57 @@ hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s)
     return hipGetLastError();
 }
 
+// Workgroup slots of the current device: 2 per compute unit (the kernel holds 2 workgroups of
+// 4 wavefronts per CU); 0 when it cannot be read.
+static int workgroup_slots()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        v = 2 * cus;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+template <int FMT>
+static void launch_form(const AccumulateArgs &a, bool split, bool narrow, hipStream_t s)
+{
+    const int rows = split ? QT : narrow ? QT / 2 : QT;
+    const dim3 grid((unsigned)(((a.M + rows - 1) / rows) * a.B * a.H));
+    if (split)
+        hipLaunchKernelGGL((accumulate_kernel<FMT, true, false>), grid, dim3(NTHR), 0, s, a);
+    else if (narrow)
+        hipLaunchKernelGGL((accumulate_kernel<FMT, false, true>), grid, dim3(NTHR), 0, s, a);
+    else
+        hipLaunchKernelGGL((accumulate_kernel<FMT, false, false>), grid, dim3(NTHR), 0, s, a);
+}
+
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s)
 {
-    const dim3 grid((unsigned)(((a.M + QT - 1) / QT) * a.B * a.H));
     // up to 64 query rows (two blocks): split the keys of every tile between wavefront pairs
     const bool split = a.M <= 2 * WQ;
-    if (kv_dtype == 0) {
-        if (split)
-            hipLaunchKernelGGL((accumulate_kernel<0, true>), grid, dim3(NTHR), 0, s, a);
-        else
-            hipLaunchKernelGGL((accumulate_kernel<0, false>), grid, dim3(NTHR), 0, s, a);
-    } else {
-        if (split)
-            hipLaunchKernelGGL((accumulate_kernel<1, true>), grid, dim3(NTHR), 0, s, a);
-        else
-            hipLaunchKernelGGL((accumulate_kernel<1, false>), grid, dim3(NTHR), 0, s, a);
+    // 128-row workgroups when 256-row ones would not fill the chip's workgroup slots, unless
+    // Q8A_ROWS_PER_WORKGROUP (128 or 256) fixes the choice
+    const int64_t wide = (int64_t)((a.M + QT - 1) / QT) * a.B * a.H;
+    bool narrow = wide < workgroup_slots();
+    if (const char *env = std::getenv("Q8A_ROWS_PER_WORKGROUP")) {
+        if (std::strcmp(env, "128") == 0)
+            narrow = true;
+        else if (std::strcmp(env, "256") == 0)
+            narrow = false;
     }
+    narrow = narrow && !split;
+    if (kv_dtype == 0)
+        launch_form<0>(a, split, narrow, s);
+    else
+        launch_form<1>(a, split, narrow, s);
     return hipGetLastError();
 }
 

@@ -106,7 +106,10 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
  *   causal   1: the triangular mask of Mode A ("Out-of-Core ...", Sec. 4); 0: every chunk key
  *            is visible to every query.
  * A row that sees no key of the chunk is left bit-for-bit untouched (tiles that lie wholly above
- * the diagonal are skipped, as in "Core Architecture ...", Sec. 5).  Each key position must be
+ * the diagonal are skipped, as in "Core Architecture ...", Sec. 5).  Workgroups take 256 query
+ * rows, or 128 when n_seq*n_heads*ceil(n_q/256) would not fill the device's workgroup slots; the
+ * environment variable Q8A_ROWS_PER_WORKGROUP=128 or 256 fixes the choice (results are the same
+ * to rounding).  Each key position must be
  * accumulated exactly once per state; chunk order is free.  Calls on one state must be
  * stream-ordered; calls on different states are independent. */
 int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, const void *v,

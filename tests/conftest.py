@@ -17,3 +17,12 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+@pytest.fixture(params=["auto", "256"])
+def rows_per_workgroup(request, monkeypatch):
+    """Run with the library's own choice of query rows per workgroup (128 for small problems)
+    and with 256 forced, so both tile forms of the accumulate kernel meet every case."""
+    if request.param != "auto":
+        monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", request.param)
+    return request.param

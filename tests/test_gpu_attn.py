@@ -55,9 +55,9 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-def test_small_cases(orc, case):
+def test_small_cases(orc, case, rows_per_workgroup):
     B, H, M, N, q_pos0, bc, causal = case
-    say("case", case)
+    say("case", case, "rows per workgroup", rows_per_workgroup)
     n_alloc = (N + 3) // 4 * 4
     assert causal or n_alloc == N  # without the mask every allocated key would be visible
     prob, qd, kd, vd = setup_case(orc, B, H, M, n_alloc, q_pos0, seed=sum(case))
@@ -67,6 +67,29 @@ def test_small_cases(orc, case):
     O_ref, lse_ref = orc.attention(prob)
     assert_close(out.float().cpu().numpy().reshape(-1, D), lse.cpu().numpy().reshape(-1),
                  O_ref, lse_ref, str(case))
+
+
+@pytest.mark.parametrize("case", [(1, 2, 200, 200, 0, 64), (2, 3, 300, 520, 220, 100),
+                                  (1, 4, 520, 520, 0, 520), (2, 2, 130, 333, 203, 100)])
+def test_row_forms_agree_bit_for_bit(orc, case, monkeypatch):
+    """128- and 256-row workgroups compute every row the same way: the same state and output
+    bits."""
+    B, H, M, N, q_pos0, bc = case
+    n_alloc = (N + 3) // 4 * 4
+    prob, qd, kd, vd = setup_case(orc, B, H, M, n_alloc, q_pos0, seed=sum(case))
+    res = {}
+    for rows in ("128", "256"):
+        monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", rows)
+        say("case", case, "rows per workgroup", rows)
+        out, lse, (m, l, o) = prefill(qd, kd, vd, q8a.KV_Q8_0, B, H, M, n_alloc, q_pos0,
+                                      chunk_list(N, bc))
+        mm = m.cpu().numpy().reshape(-1)
+        ne = ~np.isneginf(mm)
+        res[rows] = (out.cpu().numpy().view(np.uint16), lse.cpu().numpy().view(np.uint32),
+                     mm.view(np.uint32), l.cpu().numpy().view(np.uint32),
+                     o.cpu().numpy().reshape(-1, D)[ne].view(np.uint32))
+    for a, b in zip(res["128"], res["256"]):
+        assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("M", [150, 50])

@@ -31,9 +31,9 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-def test_final_rows_match_finalize(orc, case):
+def test_final_rows_match_finalize(orc, case, rows_per_workgroup):
     B, H, M, N, q_pos0, bc, kv = case
-    say("case", case)
+    say("case", case, "rows per workgroup", rows_per_workgroup)
     prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=sum(case[:6]), kv_dtype=kv)
     chunks = chunk_list(N, bc)
     out_ref, lse_ref, (m1, l1, o1) = prefill(qd, kd, vd, kv, B, H, M, N, q_pos0, chunks)
