@@ -36,6 +36,8 @@
 //     stay in that XCD's L2) and the query tiles that see the most keys start first.
 //   * Up to 64 query rows per (sequence, head) (Mode B, decode-like calls): the split-key form,
 //     where the wavefronts split every tile's keys instead of its rows (see SPLIT below).
+//   * Launches whose 256-row workgroups would not fill two slots per compute unit (one
+//     sequence of 32 heads): 128-row workgroups, one block per wavefront (see NARROW below).
 #include <hip/hip_fp16.h>
 
 #include <atomic>
@@ -809,12 +811,23 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     }
 }
 
+// m = -inf, l = 0: four rows per thread, as one 16-byte store per array when both arrays are
+// 16-byte aligned (the usual case), else four 4-byte stores
 __global__ __launch_bounds__(256) void state_init_kernel(float *m, float *l, int64_t n_rows)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n_rows) {
-        m[i] = -INFINITY;
-        l[i] = 0.f;
+    const int64_t i = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (i >= n_rows)
+        return;
+    const bool vec = ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(l)) & 15) == 0;
+    if (vec && i + 4 <= n_rows) {
+        *reinterpret_cast<float4 *>(m + i) = make_float4(-INFINITY, -INFINITY, -INFINITY,
+                                                         -INFINITY);
+        *reinterpret_cast<float4 *>(l + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    for (int64_t r = i; r < i + 4 && r < n_rows; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
     }
 }
 
@@ -903,7 +916,7 @@ __global__ __launch_bounds__(256) void merge_kernel(float *__restrict__ ma, floa
 
 hipError_t launch_state_init(float *m, float *l, int64_t n_rows, hipStream_t s)
 {
-    const int64_t grid = (n_rows + 255) / 256;
+    const int64_t grid = (n_rows + 1023) / 1024;
     hipLaunchKernelGGL(state_init_kernel, dim3((unsigned)grid), dim3(256), 0, s, m, l, n_rows);
     return hipGetLastError();
 }
@@ -944,10 +957,15 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
 {
     // up to 64 query rows (two blocks): split the keys of every tile between wavefront pairs
     const bool split = a.M <= 2 * WQ;
-    // 128-row workgroups when 256-row ones would not fill the chip's workgroup slots, unless
-    // Q8A_ROWS_PER_WORKGROUP (128 or 256) fixes the choice
+    // 128-row workgroups when 256-row ones would not fill the chip's workgroup slots and the
+    // causal diagonal crosses the chunk: the query tiles then see different numbers of keys, the
+    // launch lasts as long as the tile that sees the most, and halving the rows per workgroup
+    // halves that tile's work per key.  Where every row sees the whole chunk the load is even
+    // and the 256-row form, which unpacks each K/V tile for twice the rows, is a little faster.
+    // Q8A_ROWS_PER_WORKGROUP (128 or 256) fixes the choice.
     const int64_t wide = (int64_t)((a.M + QT - 1) / QT) * a.B * a.H;
-    bool narrow = wide < workgroup_slots();
+    const bool diagonal = a.causal && a.q_pos0 < a.kv_pos0 + a.n_kv - 1;
+    bool narrow = diagonal && wide < workgroup_slots();
     if (const char *env = std::getenv("Q8A_ROWS_PER_WORKGROUP")) {
         if (std::strcmp(env, "128") == 0)
             narrow = true;

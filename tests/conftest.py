@@ -19,10 +19,10 @@ def orc():
     return oracle
 
 
-@pytest.fixture(params=["auto", "256"])
+@pytest.fixture(params=["128", "256"])
 def rows_per_workgroup(request, monkeypatch):
-    """Run with the library's own choice of query rows per workgroup (128 for small problems)
-    and with 256 forced, so both tile forms of the accumulate kernel meet every case."""
-    if request.param != "auto":
-        monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", request.param)
+    """Run with 128 and with 256 query rows per workgroup forced, so both tile forms of the
+    accumulate kernel meet every case (tests without this fixture run the library's own
+    choice)."""
+    monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", request.param)
     return request.param
