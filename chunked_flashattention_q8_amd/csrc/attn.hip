@@ -168,7 +168,11 @@ struct Smem {
 };
 
 // Unpack the raw rows of one KV tile (LDS) into MFMA operand layout (LDS).  All 256 threads.
-template <int FMT>
+// MASK: Q8_0 keys from valid_keys on get zero scales.  The bytes of a 16-byte piece that runs
+// past the chunk end are real memory (see the range rounding in the kernel); when the chunk's
+// byte length is a multiple of 16 there is no such piece, every byte past the end reads as 0,
+// and those keys unpack to zero scales by themselves.
+template <int FMT, bool MASK>
 __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                                             const uint8_t *__restrict__ rv, KvTile<FMT> &T,
                                             int tid, int valid_keys)
@@ -210,7 +214,7 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             const float r0 = d0 * rcp;
             const float kr = __builtin_fmaf(__builtin_fmaf(-den, r0, d0), rcp, r0);
             const float sc = (qq & 1) ? den * kScaleLog2 : kr;
-            ((qq & 1) ? T.km : T.kr)[key] = key < valid_keys ? sc : 0.f;
+            ((qq & 1) ? T.km : T.kr)[key] = (!MASK || key < valid_keys) ? sc : 0.f;
         }
         { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
             // dims 4*dg .. 4*dg+3 sit at byte 2 + 4*dg + 2*blk of the row (block 1 skips the
@@ -231,7 +235,7 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             for (int c = 0; c < 4; ++c) {
                 const _Float16 d =
                     *reinterpret_cast<const _Float16 *>(rv + (4 * kq + c) * 68 + 34 * blk);
-                sc[c] = 4 * kq + c < valid_keys ? d : (_Float16)0.0f;
+                sc[c] = (!MASK || 4 * kq + c < valid_keys) ? d : (_Float16)0.0f;
             }
             const half2v s01 = {sc[0], sc[1]}, s23 = {sc[2], sc[3]};
             // byte transpose: t01[i] interleaves the bytes of keys 0 and 1 for dims 2i, 2i+1
@@ -286,7 +290,9 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
 // NARROW (used when 256-row workgroups would leave compute-unit slots empty, e.g. one sequence
 // of 32 heads): a workgroup takes 128 query rows, wavefront w the 32-row block w over all keys,
 // so twice as many workgroups share the chip; each K/V tile is unpacked for half as many rows.
-template <int FMT, bool SPLIT, bool NARROW>
+// CLEAN: the chunk's rows end on a 16-byte boundary (n_kv a multiple of 4 for Q8_0, always for
+// FP16), so the unpack needs no masking of keys past the chunk end.
+template <int FMT, bool SPLIT, bool NARROW, bool CLEAN>
 __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 {
     static_assert(!(SPLIT && NARROW), "one form at a time");
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     }
     __builtin_amdgcn_s_waitcnt(0); // the copies have landed in LDS before the barrier
     __syncthreads();
-    unpack_tile<FMT>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
+    unpack_tile<FMT, !CLEAN>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     }
                 }
             // independent VALU work for the matrix instructions above to overlap with
-            unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
+            unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
 
             // u = S*log2(e)/8 - ref, the exponent relative to the reference maximum before
@@ -674,7 +680,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     }
             }
         } else {
-            unpack_tile<FMT>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
+            unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
         }
         __builtin_amdgcn_s_waitcnt(0); // raw rows of tile t+2 have landed before the barrier
@@ -940,17 +946,29 @@ static int workgroup_slots()
     return v;
 }
 
-template <int FMT>
+// Launches the query tiles whose rows see some key of the chunk: with the causal mask, rows before
+// position kv_pos0 see none, and the kernel maps the first workgroups to the last query tiles, so
+// the grid ends at the first tile that holds a row at or past kv_pos0.
+template <int FMT, bool CLEAN>
 static void launch_form(const AccumulateArgs &a, bool split, bool narrow, hipStream_t s)
 {
     const int rows = split ? QT : narrow ? QT / 2 : QT;
-    const dim3 grid((unsigned)(((a.M + rows - 1) / rows) * a.B * a.H));
+    const int64_t n_qt = (a.M + rows - 1) / rows;
+    int64_t first_row = 0;
+    if (a.causal && a.kv_pos0 > a.q_pos0)
+        first_row = a.kv_pos0 - a.q_pos0;
+    if (first_row >= a.M)
+        return; // no row sees the chunk
+    const dim3 grid((unsigned)((n_qt - first_row / rows) * a.B * a.H));
     if (split)
-        hipLaunchKernelGGL((accumulate_kernel<FMT, true, false>), grid, dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL((accumulate_kernel<FMT, true, false, CLEAN>), grid, dim3(NTHR), 0, s,
+                           a);
     else if (narrow)
-        hipLaunchKernelGGL((accumulate_kernel<FMT, false, true>), grid, dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL((accumulate_kernel<FMT, false, true, CLEAN>), grid, dim3(NTHR), 0, s,
+                           a);
     else
-        hipLaunchKernelGGL((accumulate_kernel<FMT, false, false>), grid, dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL((accumulate_kernel<FMT, false, false, CLEAN>), grid, dim3(NTHR), 0, s,
+                           a);
 }
 
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s)
@@ -973,10 +991,12 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
             narrow = false;
     }
     narrow = narrow && !split;
-    if (kv_dtype == 0)
-        launch_form<0>(a, split, narrow, s);
+    if (kv_dtype != 0)
+        launch_form<1, true>(a, split, narrow, s); // FP16 rows: 128 bytes, always clean
+    else if (a.n_kv % 4 == 0)
+        launch_form<0, true>(a, split, narrow, s);
     else
-        launch_form<1>(a, split, narrow, s);
+        launch_form<0, false>(a, split, narrow, s);
     return hipGetLastError();
 }
 
