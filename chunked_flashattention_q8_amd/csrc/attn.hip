@@ -43,6 +43,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "q8attn_internal.h"
 
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         }
     };
 
-    auto tile = [&](const int t) {
+    auto tile = [&](const int t, auto jlo_c) {
         // raw buffer t&1 was unpacked in the previous interval; no copies past the last tile
         // (for a workgroup on the causal diagonal they would be real reads)
         if (t + 2 < n_tiles)
@@ -510,175 +511,180 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         const int key0 = t * KT;
         // tile t+1 is unpacked from its raw rows in every branch: the same barrier interval
         // that reads operand buffer t&1 writes buffer (t+1)&1
-        if (key0 < kv_end_w) {
-            // S^T = K Q^T: lane (qcol, g) holds
-            // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][si][v], sub the
-            // si-th key subtile this wavefront covers.  Q8_0: the first block's products (dims
-            // 0-31) are scaled by kr before the second block's are added.
-            floatx16 s[NJ][NS];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int si = 0; si < NS; ++si)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        s[j][si][v] = 0.f;
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
+        // the tile's work for blocks JLO .. NJ-1 (JLO = 1: block 0 sees no key of this tile)
+        auto compute = [&](auto jlo_c) {
+            constexpr int JLO = decltype(jlo_c)::value;
+                // S^T = K Q^T: lane (qcol, g) holds
+                // S^T[key 32*sub + 8*(v/4) + 4*g + v%4][query qcol] in s[j][si][v], sub the
+                // si-th key subtile this wavefront covers.  Q8_0: the first block's products (dims
+                // 0-31) are scaled by kr before the second block's are added.
+                floatx16 s[NJ][NS];
+    #pragma unroll
+                for (int j = JLO; j < NJ; ++j)
+    #pragma unroll
+                    for (int si = 0; si < NS; ++si)
+    #pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            s[j][si][v] = 0.f;
+    #pragma unroll
+                for (int half = 0; half < 2; ++half)
+    #pragma unroll
+                    for (int si = 0; si < NS; ++si) {
+                        const int sub = SPLIT ? kh : si;
+                        const int krow = (32 * sub + qcol) * KP + 8 * g;
+                        if (FMT == 0 && half == 1) {
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float4 r4 =
+                                    *reinterpret_cast<const float4 *>(&T.kr[32 * sub + 8 * i + 4 * g]);
+    #pragma unroll
+                                for (int j = JLO; j < NJ; ++j) {
+                                    s[j][si][4 * i + 0] *= r4.x;
+                                    s[j][si][4 * i + 1] *= r4.y;
+                                    s[j][si][4 * i + 2] *= r4.z;
+                                    s[j][si][4 * i + 3] *= r4.w;
+                                }
+                            }
+                        }
+    #pragma unroll
+                        for (int kk = 2 * half; kk < 2 * half + 2; ++kk) {
+                            const half8 ak = *reinterpret_cast<const half8 *>(&T.k[krow + 16 * kk]);
+    #pragma unroll
+                            for (int j = JLO; j < NJ; ++j)
+                                s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[j][kk],
+                                                                                 s[j][si], 0, 0, 0);
+                        }
+                    }
+                // independent VALU work for the matrix instructions above to overlap with
+                unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
+                                 sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
+
+                // u = S*log2(e)/8 - ref, the exponent relative to the reference maximum before
+                // this tile (0 while it is -inf)
+                float base[NJ];
+    #pragma unroll
+                for (int j = JLO; j < NJ; ++j)
+                    base[j] = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
+    #pragma unroll
                 for (int si = 0; si < NS; ++si) {
                     const int sub = SPLIT ? kh : si;
-                    const int krow = (32 * sub + qcol) * KP + 8 * g;
-                    if (FMT == 0 && half == 1) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float4 r4 =
-                                *reinterpret_cast<const float4 *>(&T.kr[32 * sub + 8 * i + 4 * g]);
-#pragma unroll
-                            for (int j = 0; j < NJ; ++j) {
-                                s[j][si][4 * i + 0] *= r4.x;
-                                s[j][si][4 * i + 1] *= r4.y;
-                                s[j][si][4 * i + 2] *= r4.z;
-                                s[j][si][4 * i + 3] *= r4.w;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float4 m4 = {kScaleLog2, kScaleLog2, kScaleLog2, kScaleLog2};
+                        if constexpr (FMT == 0)
+                            m4 = *reinterpret_cast<const float4 *>(&T.km[32 * sub + 8 * i + 4 * g]);
+    #pragma unroll
+                        for (int j = JLO; j < NJ; ++j) {
+                            s[j][si][4 * i + 0] = __builtin_fmaf(s[j][si][4 * i + 0], m4.x, -base[j]);
+                            s[j][si][4 * i + 1] = __builtin_fmaf(s[j][si][4 * i + 1], m4.y, -base[j]);
+                            s[j][si][4 * i + 2] = __builtin_fmaf(s[j][si][4 * i + 2], m4.z, -base[j]);
+                            s[j][si][4 * i + 3] = __builtin_fmaf(s[j][si][4 * i + 3], m4.w, -base[j]);
+                        }
+                    }
+                }
+
+                // The 32-key subtiles that some row of a block cannot wholly see (causal diagonal,
+                // ragged chunk end, padding rows) are masked element by element; the common case
+                // skips this with one wavefront-uniform test.
+                if (key0 + KT > kv_full_w) {
+    #pragma unroll
+                    for (int j = JLO; j < NJ; ++j) {
+                        // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
+                        const int rel = lim[j] - key0 - 4 * g;
+    #pragma unroll
+                        for (int si = 0; si < NS; ++si) {
+                            const int sub = SPLIT ? kh : si;
+                            if (key0 + 32 * sub + 32 > kv_full_b[j]) {
+    #pragma unroll
+                                for (int v = 0; v < 16; ++v)
+                                    s[j][si][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
+                                                      ? s[j][si][v] : -INFINITY;
                             }
                         }
                     }
-#pragma unroll
-                    for (int kk = 2 * half; kk < 2 * half + 2; ++kk) {
-                        const half8 ak = *reinterpret_cast<const half8 *>(&T.k[krow + 16 * kk]);
-#pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[j][kk],
-                                                                             s[j][si], 0, 0, 0);
-                    }
                 }
-            // independent VALU work for the matrix instructions above to overlap with
-            unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
-                             sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
-
-            // u = S*log2(e)/8 - ref, the exponent relative to the reference maximum before
-            // this tile (0 while it is -inf)
-            float base[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                base[j] = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
-#pragma unroll
-            for (int si = 0; si < NS; ++si) {
-                const int sub = SPLIT ? kh : si;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float4 m4 = {kScaleLog2, kScaleLog2, kScaleLog2, kScaleLog2};
-                    if constexpr (FMT == 0)
-                        m4 = *reinterpret_cast<const float4 *>(&T.km[32 * sub + 8 * i + 4 * g]);
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        s[j][si][4 * i + 0] = __builtin_fmaf(s[j][si][4 * i + 0], m4.x, -base[j]);
-                        s[j][si][4 * i + 1] = __builtin_fmaf(s[j][si][4 * i + 1], m4.y, -base[j]);
-                        s[j][si][4 * i + 2] = __builtin_fmaf(s[j][si][4 * i + 2], m4.z, -base[j]);
-                        s[j][si][4 * i + 3] = __builtin_fmaf(s[j][si][4 * i + 3], m4.w, -base[j]);
-                    }
-                }
-            }
-
-            // The 32-key subtiles that some row of a block cannot wholly see (causal diagonal,
-            // ragged chunk end, padding rows) are masked element by element; the common case
-            // skips this with one wavefront-uniform test.
-            if (key0 + KT > kv_full_w) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
-                    const int rel = lim[j] - key0 - 4 * g;
-#pragma unroll
-                    for (int si = 0; si < NS; ++si) {
-                        const int sub = SPLIT ? kh : si;
-                        if (key0 + 32 * sub + 32 > kv_full_b[j]) {
-#pragma unroll
-                            for (int v = 0; v < 16; ++v)
-                                s[j][si][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
-                                                  ? s[j][si][v] : -INFINITY;
+                bool need_any = false;
+                float mx[NJ];
+                bool need[NJ];
+    #pragma unroll
+                for (int j = JLO; j < NJ; ++j) {
+                    if constexpr (NS == 2) {
+                        float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
+                        float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
+    #pragma unroll
+                        for (int v = 3; v < 15; v += 2) {
+                            ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
+                            mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
                         }
+                        mx[j] = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
+                    } else {
+                        float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
+    #pragma unroll
+                        for (int v = 3; v < 15; v += 2)
+                            ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
+                        mx[j] = fmaxf(ma, s[j][0][15]);
+                    }
+                    mx[j] = half_swap_max(mx[j]); // tile maximum of u for this query row
+                    m_top[j] = fmaxf(m_top[j], base[j] + mx[j]);
+                    saw[j] = saw[j] || (mx[j] != -INFINITY);
+                    // raise the reference when the tile's maximum exceeds it by more than kTau (or
+                    // when it is still -inf and the row saw a key)
+                    need[j] = mx[j] > (m_ref[j] == -INFINITY ? -INFINITY : kTau);
+                    need_any = need_any || need[j];
+                }
+                if (__builtin_amdgcn_ballot_w64(need_any)) {
+    #pragma unroll
+                    for (int j = JLO; j < NJ; ++j) {
+                        const float delta = need[j] ? mx[j] : 0.f; // new ref = base + delta
+                        const float alpha = (m_ref[j] == -INFINITY)
+                                                ? 0.f : __builtin_amdgcn_exp2f(-delta);
+                        l_part[j] *= alpha;
+                        o[j][0] *= alpha;
+                        o[j][1] *= alpha;
+                        if (need[j])
+                            m_ref[j] = base[j] + delta;
+    #pragma unroll
+                        for (int si = 0; si < NS; ++si)
+                            s[j][si] -= delta;
                     }
                 }
-            }
-            bool need_any = false;
-            float mx[NJ];
-            bool need[NJ];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                if constexpr (NS == 2) {
-                    float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
-                    float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
-#pragma unroll
-                    for (int v = 3; v < 15; v += 2) {
-                        ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
-                        mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
+                // per query block: P = exp2(u) (l sums the FP32 values), P to FP16, then
+                // O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
+    #pragma unroll
+                for (int j = JLO; j < NJ; ++j) {
+                    float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
+                    half8 p16[NS][2];
+    #pragma unroll
+                    for (int si = 0; si < NS; ++si) {
+    #pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const float p = __builtin_amdgcn_exp2f(s[j][si][v]);
+                            s[j][si][v] = p;
+                            ls[v & 3] += p;
+                        }
+                        p16[si][0] = to_half8(s[j][si], 0);
+                        p16[si][1] = to_half8(s[j][si], 8);
                     }
-                    mx[j] = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
-                } else {
-                    float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
-#pragma unroll
-                    for (int v = 3; v < 15; v += 2)
-                        ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
-                    mx[j] = fmaxf(ma, s[j][0][15]);
-                }
-                mx[j] = half_swap_max(mx[j]); // tile maximum of u for this query row
-                m_top[j] = fmaxf(m_top[j], base[j] + mx[j]);
-                saw[j] = saw[j] || (mx[j] != -INFINITY);
-                // raise the reference when the tile's maximum exceeds it by more than kTau (or
-                // when it is still -inf and the row saw a key)
-                need[j] = mx[j] > (m_ref[j] == -INFINITY ? -INFINITY : kTau);
-                need_any = need_any || need[j];
-            }
-            if (__builtin_amdgcn_ballot_w64(need_any)) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const float delta = need[j] ? mx[j] : 0.f; // new ref = base + delta
-                    const float alpha = (m_ref[j] == -INFINITY)
-                                            ? 0.f : __builtin_amdgcn_exp2f(-delta);
-                    l_part[j] *= alpha;
-                    o[j][0] *= alpha;
-                    o[j][1] *= alpha;
-                    if (need[j])
-                        m_ref[j] = base[j] + delta;
-#pragma unroll
+                    l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+                    // the V tile's key order matches the accumulator layout
+    #pragma unroll
                     for (int si = 0; si < NS; ++si)
-                        s[j][si] -= delta;
+    #pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) {
+                            const int sub = SPLIT ? kh : si;
+                            const int pos = 32 * sub + 16 * tt + 8 * g;
+                            const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
+                            const half8 a1 =
+                                *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
+                            o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p16[si][tt],
+                                                                             o[j][0], 0, 0, 0);
+                            o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p16[si][tt],
+                                                                             o[j][1], 0, 0, 0);
+                        }
                 }
-            }
-            // per query block: P = exp2(u) (l sums the FP32 values), P to FP16, then
-            // O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
-                half8 p16[NS][2];
-#pragma unroll
-                for (int si = 0; si < NS; ++si) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const float p = __builtin_amdgcn_exp2f(s[j][si][v]);
-                        s[j][si][v] = p;
-                        ls[v & 3] += p;
-                    }
-                    p16[si][0] = to_half8(s[j][si], 0);
-                    p16[si][1] = to_half8(s[j][si], 8);
-                }
-                l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-                // the V tile's key order matches the accumulator layout
-#pragma unroll
-                for (int si = 0; si < NS; ++si)
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const int sub = SPLIT ? kh : si;
-                        const int pos = 32 * sub + 16 * tt + 8 * g;
-                        const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
-                        const half8 a1 =
-                            *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
-                        o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p16[si][tt],
-                                                                         o[j][0], 0, 0, 0);
-                        o[j][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, p16[si][tt],
-                                                                         o[j][1], 0, 0, 0);
-                    }
-            }
+        };
+        if (key0 < kv_end_w) {
+            compute(jlo_c);
         } else {
             unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
                              sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
@@ -689,9 +695,25 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     // The first tile is peeled: the state loads are issued right before its copies, so the
     // wait in front of their first use leaves those copies in flight.
     load_resumed();
-    tile(0);
-    for (int t = 1; t < n_tiles; ++t)
-        tile(t);
+    tile(0, std::integral_constant<int, 0>{});
+    if constexpr (NJ == 2 && (CLEAN || FMT == 1)) {
+        // On the causal diagonal a wavefront's first block (the lower rows) stops seeing keys
+        // before its second block does; from then on the tiles run for the second block only
+        // (the work left out would be all masked).  Each wavefront runs every tile interval, so
+        // the barriers still match.  (Not in the masked Q8_0 unpack form: there the second loop
+        // would push the kernel past 256 VGPRs.)
+        int t_two = n_tiles;
+        if (kv_end_b[1] > kv_end_b[0])
+            t_two = max(1, (kv_end_b[0] + KT - 1) / KT);
+        int t = 1;
+        for (; t < t_two; ++t)
+            tile(t, std::integral_constant<int, 0>{});
+        for (; t < n_tiles; ++t)
+            tile(t, std::integral_constant<int, 1>{});
+    } else {
+        for (int t = 1; t < n_tiles; ++t)
+            tile(t, std::integral_constant<int, 0>{});
+    }
 
     if constexpr (SPLIT) {
         // merge the two key subtiles' states of each block: the second subtile's wavefront
