@@ -68,6 +68,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kScaleLog2 = 0.125f * kLog2e; // 1/sqrt(64) * log2(e)
 constexpr float kTau = 8.0f; // lazy rescale threshold, log2 units
+// s_waitcnt operand: vmcnt <= 2, expcnt and lgkmcnt not waited for (their fields at maximum)
+constexpr int kWaitVm2 = 2 | (7 << 4) | (15 << 8);
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -423,12 +425,10 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     // Loads past the chunk read as zero, and operand tiles unpacked from raw rows past the last
     // tile are never read, so unpack runs unconditionally (no branches inside the tile loop's
     // scheduling regions); copies are skipped past the last tile.
-    // Prologue: the first two tiles' copies, then every row's Q and m, all in flight together;
-    // the resumed rows' l and O are loaded after it, their latency covered by the first tile's
-    // QK work (they are first used by its rescale or PV products).
+    // Prologue: tile 0's copies, every row's Q and m, then tile 1's copies, all in flight
+    // together; the resumed rows' l and O are loaded after it, their latency covered by the
+    // first tile's QK work (they are first used by its rescale or PV products).
     fetch(0, 0);
-    if (n_tiles > 1)
-        fetch(1, 1);
 
     half8 qreg[NJ][4];
     floatx16 o[NJ][2];
@@ -462,9 +462,18 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                 qreg[j][kk] = half8{};
         }
     }
-    __builtin_amdgcn_s_waitcnt(0); // the copies have landed in LDS before the barrier
+    // Tile 1's copies go last: at least two per thread (slots 0 and 1), so waiting until at
+    // most two vector-memory loads are outstanding (they complete in order) leaves only those
+    // in flight while tile 0 is unpacked; they have landed before the barrier after it.
+    if (n_tiles > 1) {
+        fetch(1, 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);
+    }
     __syncthreads();
     unpack_tile<FMT, !CLEAN>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
