@@ -70,6 +70,10 @@ constexpr float kScaleLog2 = 0.125f * kLog2e; // 1/sqrt(64) * log2(e)
 constexpr float kTau = 8.0f; // lazy rescale threshold, log2 units
 // s_waitcnt operand: vmcnt <= 2, expcnt and lgkmcnt not waited for (their fields at maximum)
 constexpr int kWaitVm2 = 2 | (7 << 4) | (15 << 8);
+// cache policy of the write-back's buffer stores: sc0 | sc1 (system scope), written through the
+// XCD's L2 instead of left dirty in it, so the end-of-launch L2 write-back before the next call
+// has less to do (the next call reads the rows from the memory-side cache either way)
+constexpr int kStoreThrough = 1 | 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -805,13 +809,15 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                 stg_l[qcol] = l_st;
             }
             const uint32_t ml_off = (wr && g == 0) ? (q0 + qcol) * 4u : kNoRow;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_st), rs_m, ml_off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_st), rs_l, ml_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_st), rs_m, ml_off, 0,
+                                                  kStoreThrough);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_st), rs_l, ml_off, 0,
+                                                  kStoreThrough);
             if (fin_block && a.lse)
                 __builtin_amdgcn_raw_buffer_store_b32(
                     __float_as_uint(m_st + logf(l_st)),
                     make_rsrc(a.lse + head * a.M, (uint32_t)a.M * 4u),
-                    (fin && g == 0) ? (q0 + qcol) * 4u : kNoRow, 0, 0);
+                    (fin && g == 0) ? (q0 + qcol) * 4u : kNoRow, 0, kStoreThrough);
             // the same wavefront reads back what it wrote (LDS keeps a wavefront's order): all
             // rows and flags first, so the LDS reads overlap, then the stores
             u32x4 vv[WQ / 4];
@@ -824,7 +830,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             }
 #pragma unroll
             for (int i = 0; i < WQ / 4; ++i)
-                __builtin_amdgcn_raw_buffer_store_b128(vv[i], rs_o, off[i], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(vv[i], rs_o, off[i], 0, kStoreThrough);
             if (fin_block) {
                 // out = O / l rounded once to FP16, 4 values per lane and row
                 const __amdgpu_buffer_rsrc_t rs_out =
@@ -841,7 +847,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                                      (_Float16)(__uint_as_float(vv[i][2]) / lv),
                                      (_Float16)(__uint_as_float(vv[i][3]) / lv)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rs_out,
-                                                          oo, 0, 0);
+                                                          oo, 0, kStoreThrough);
                 }
             }
         }
