@@ -4,6 +4,7 @@
 // HBM-bound: each 32-value block reads 128 bytes and writes 34.  Eight consecutive lanes own one
 // block and each loads one 16-byte float4, so a wavefront reads 1 KiB of contiguous input per
 // instruction; every lane handles two blocks, 256 float4 apart, with both loads in flight.  The
+// loads are non-temporal (the source is read once).  The
 // block's largest magnitude is reduced over the eight lanes, every lane derives the same FP16
 // scale, quantises its four values and writes them as two 16-bit stores (block starts are 2-byte
 // aligned: 34 * k).
@@ -19,6 +20,8 @@
 
 namespace q8a {
 namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // round(x / dh), halves away from zero, clamped to [-127, 127], with x / dh the correctly
 // rounded FP32 quotient z'.  rdh is the hardware reciprocal of dh (relative error at most 2^-23):
@@ -71,7 +74,11 @@ __global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict
     for (int u = 0; u < U; ++u) {
         const int64_t gid = ((int64_t)blockIdx.x * U + u) * 256 + threadIdx.x;
         blk[u] = gid >> 3;
-        v[u] = blk[u] < n_blocks ? x[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
+        // the FP32 source is read once: non-temporal loads keep it from displacing cached data
+        floatx4 t = {0.f, 0.f, 0.f, 0.f};
+        if (blk[u] < n_blocks)
+            t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(x) + gid);
+        v[u] = make_float4(t.x, t.y, t.z, t.w);
     }
     const int sub = (int)(threadIdx.x & 7);
 #pragma unroll
