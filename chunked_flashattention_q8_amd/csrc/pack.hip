@@ -3,8 +3,8 @@
 //
 // HBM-bound: each 32-value block reads 128 bytes and writes 34.  Eight consecutive lanes own one
 // block and each loads one 16-byte float4, so a wavefront reads 1 KiB of contiguous input per
-// instruction; every lane handles two blocks, 256 float4 apart, with both loads in flight.  The
-// loads are non-temporal (the source is read once).  The
+// instruction; every lane handles two blocks, 256 float4 apart, with both loads in flight.  Loads
+// and stores are non-temporal (the source is read once; the packed rows are streamed out).  The
 // block's largest magnitude is reduced over the eight lanes, every lane derives the same FP16
 // scale, quantises its four values and writes them as two 16-bit stores (block starts are 2-byte
 // aligned: 34 * k).
@@ -95,11 +95,14 @@ __global__ __launch_bounds__(256) void q8_0_pack_kernel(const float4 *__restrict
         const int q2 = quantise(v[u].z, dh, rdh), q3 = quantise(v[u].w, dh, rdh);
         if (blk[u] < n_blocks) {
             uint8_t *out = dst + blk[u] * 34;
-            if (sub == 0)
-                *reinterpret_cast<uint16_t *>(out) = __half_as_ushort(d16);
+            // non-temporal stores: streamed out, not kept in the L2 for the end-of-launch
+            // write-back
             uint16_t *o16 = reinterpret_cast<uint16_t *>(out + 2 + 4 * sub);
-            o16[0] = (uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8));
-            o16[1] = (uint16_t)((q2 & 0xff) | ((q3 & 0xff) << 8));
+            if (sub == 0)
+                __builtin_nontemporal_store(__half_as_ushort(d16),
+                                            reinterpret_cast<uint16_t *>(out));
+            __builtin_nontemporal_store((uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8)), o16);
+            __builtin_nontemporal_store((uint16_t)((q2 & 0xff) | ((q3 & 0xff) << 8)), o16 + 1);
         }
     }
 }
