@@ -746,8 +746,8 @@ def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mib,
     of cal_mib MiB, which scales each counter to bytes."""
     import synthetic
     w = synthetic.WORKLOADS[2]
-    fetch, n_f = counter_means(fetch_dir, "FETCH_SIZE", "accumulate_kernel<0, false, false, true>")
-    write, n_w = counter_means(write_dir, "WRITE_SIZE", "accumulate_kernel<0, false, false, true>")
+    fetch, n_f = counter_means(fetch_dir, "FETCH_SIZE", "accumulate_kernel<0, 0, true>")
+    write, n_w = counter_means(write_dir, "WRITE_SIZE", "accumulate_kernel<0, 0, true>")
     cf, _ = counter_means(cal_fetch_dir, "FETCH_SIZE", "copy")
     cw, _ = counter_means(cal_write_dir, "WRITE_SIZE", "copy")
     copy_bytes = cal_mib * (1 << 20)
@@ -755,7 +755,7 @@ def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mib,
     hbm = fetch * 1024 * f_fac + write * 1024 * w_fac
     alg = algorithmic_bytes(w, w.chunk)
     lines = [
-        "# HBM traffic of accumulate_kernel<0, false, false, true> (Q8_0 KV, the 256-row prefill form) per launch, batch8_m2048 workload:",
+        "# HBM traffic of accumulate_kernel<0, 0, true> (Q8_0 KV, the 256-row prefill form) per launch, batch8_m2048 workload:",
         "# 8 sequences x 32 heads, M = N = 2048 causal, d = 64, B_C = 512 (4 launches per step,",
         "# each also writing out and lse of the rows whose position lies in its chunk).",
         "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, averaged over the accumulate dispatches;",

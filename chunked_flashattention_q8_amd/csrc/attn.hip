@@ -62,14 +62,18 @@ constexpr int QT = 256;  // query rows per workgroup (4 wavefronts x 2 blocks of
 constexpr int WQ = 32;   // query rows per MFMA block
 constexpr int KT = 64;   // keys per LDS tile
 constexpr int NTHR = 256;
+// tile forms of the accumulate kernel (its FORM argument); see the kernel
+constexpr int kWide = 0;     // 256 rows, 4 wavefronts, blocks w and 7 - w over all keys
+constexpr int kSplit = 1;    // up to 64 rows, 4 wavefronts, block w & 1 over key half w >> 1
+constexpr int kNarrow = 2;   // 128 rows, 4 wavefronts, block w over all keys
+constexpr int kKeySplit = 3; // 256 rows, 8 wavefronts, blocks w & 3 and 7 - (w & 3) over key
+                             // half w >> 2
 constexpr int KP = 72;   // LDS pitch (halves) of the K tiles (144-byte rows)
 constexpr int VP = 72;   // LDS pitch (halves) of the transposed V tile
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kScaleLog2 = 0.125f * kLog2e; // 1/sqrt(64) * log2(e)
 constexpr float kTau = 8.0f; // lazy rescale threshold, log2 units
-// s_waitcnt operand: vmcnt <= 2, expcnt and lgkmcnt not waited for (their fields at maximum)
-constexpr int kWaitVm2 = 2 | (7 << 4) | (15 << 8);
 // cache policy of the write-back's buffer stores: sc0 | sc1 (system scope), written through the
 // XCD's L2 instead of left dirty in it, so the end-of-launch L2 write-back before the next call
 // has less to do (the next call reads the rows from the memory-side cache either way)
@@ -174,18 +178,20 @@ struct Smem {
     KvTile<FMT> tile[2];
 };
 
-// Unpack the raw rows of one KV tile (LDS) into MFMA operand layout (LDS).  All 256 threads.
+// Unpack the raw rows of one KV tile (LDS) into MFMA operand layout (LDS), with 256 threads
+// (tid 0-255): PART 0 both tensors, 1 K only, 2 V only.
 // MASK: Q8_0 keys from valid_keys on get zero scales.  The bytes of a 16-byte piece that runs
 // past the chunk end are real memory (see the range rounding in the kernel); when the chunk's
 // byte length is a multiple of 16 there is no such piece, every byte past the end reads as 0,
 // and those keys unpack to zero scales by themselves.
-template <int FMT, bool MASK>
+template <int FMT, bool MASK, int PART = 0>
 __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
                                             const uint8_t *__restrict__ rv, KvTile<FMT> &T,
                                             int tid, int valid_keys)
 {
     if constexpr (FMT == 0) {
-        { // K: thread = (key, quarter of the dims); quarter qq = dims 16qq .. 16qq+15, which
+        if constexpr (PART != 2) {
+            // K: thread = (key, quarter of the dims); quarter qq = dims 16qq .. 16qq+15, which
             // sit at byte 34*blk + 2 + 16*hh of the row (blk = qq/2, hh = qq%2): read the 5 dwords
             // that cover them and realign (by 2 bytes for block 0, none for block 1).
             const int key = tid >> 2, qq = tid & 3, blk = qq >> 1, hh = qq & 1;
@@ -223,7 +229,7 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             const float sc = (qq & 1) ? den * kScaleLog2 : kr;
             ((qq & 1) ? T.km : T.kr)[key] = (!MASK || key < valid_keys) ? sc : 0.f;
         }
-        { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
+        if constexpr (PART != 1) { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
             // dims 4*dg .. 4*dg+3 sit at byte 2 + 4*dg + 2*blk of the row (block 1 skips the
             // second scale): realign by 2 bytes for block 0, none for block 1
             const int kq = tid & 15, dg = tid >> 4, blk = dg >> 3;
@@ -266,14 +272,14 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             }
         }
     } else {
-        { // K: straight copy into the padded tile
+        if constexpr (PART != 2) { // K: straight copy into the padded tile
             const int key = tid >> 2, qq = tid & 3;
             const u32x4 *src = reinterpret_cast<const u32x4 *>(rk + key * 128 + 32 * qq);
             u32x4 *dst = reinterpret_cast<u32x4 *>(&T.k[key * KP + 16 * qq]);
             dst[0] = src[0];
             dst[1] = src[1];
         }
-        { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
+        if constexpr (PART != 1) { // V: thread = (4 keys, 4 dims); transposed to [dim][vpos(key)]
             const int kq = tid & 15, dg = tid >> 4;
             half4 x[4];
 #pragma unroll
@@ -297,18 +303,29 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
 // NARROW (used when 256-row workgroups would leave compute-unit slots empty, e.g. one sequence
 // of 32 heads): a workgroup takes 128 query rows, wavefront w the 32-row block w over all keys,
 // so twice as many workgroups share the chip; each K/V tile is unpacked for half as many rows.
+// KEY SPLIT (used when 256-row workgroups would leave compute-unit slots empty and every row
+// sees the whole chunk, e.g. the cached chunks of one sequence's long context): 8 wavefronts,
+// one workgroup per compute unit; wavefronts w and w + 4 own the same two blocks as wavefront w
+// of the 256-row form and split every tile's keys (w >> 2: key half), each with a state of its
+// own, merged through LDS at the end as in SPLIT.  The SIMDs then run two wavefronts each, and
+// each K/V tile is still unpacked once for 256 rows (K by wavefronts 0-3, V by 4-7).
 // CLEAN: the chunk's rows end on a 16-byte boundary (n_kv a multiple of 4 for Q8_0, always for
 // FP16), so the unpack needs no masking of keys past the chunk end.
-template <int FMT, bool SPLIT, bool NARROW, bool CLEAN>
-__global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
+template <int FMT, int FORM, bool CLEAN>
+__global__ __launch_bounds__(FORM == kKeySplit ? 2 * NTHR : NTHR, FORM == kKeySplit ? 1 : 2)
+void accumulate_kernel(AccumulateArgs a)
 {
-    static_assert(!(SPLIT && NARROW), "one form at a time");
+    constexpr bool SPLIT = FORM == kSplit, NARROW = FORM == kNarrow, KS8 = FORM == kKeySplit;
+    constexpr bool KSPLIT = SPLIT || KS8;        // wavefronts split every tile's keys
     constexpr int NJ = (SPLIT || NARROW) ? 1 : 2; // 32-row query blocks per wavefront
-    constexpr int NS = SPLIT ? 1 : 2;             // 32-key subtiles per wavefront and tile
+    constexpr int NS = KSPLIT ? 1 : 2;            // 32-key subtiles per wavefront and tile
     constexpr int QTF = NARROW ? QT / 2 : QT;     // query rows per workgroup
     constexpr int ROW = Smem<FMT>::ROW;
     constexpr int RAW16 = KT * ROW / 16;                 // 16-byte pieces per tensor tile
-    constexpr int NPRE = FMT == 0 ? 3 : 4;               // prefetch slots per thread
+    constexpr int NPRE = KS8 ? 2 : FMT == 0 ? 3 : 4;     // prefetch slots per thread
+    // the fewest copies of a tile any thread issues (the prologue's wait counts on them)
+    constexpr int kTileCopiesMin = (KS8 && FMT == 0) ? 1 : 2;
+    constexpr int kWaitTile1 = kTileCopiesMin | (7 << 4) | (15 << 8); // s_waitcnt vmcnt(min)
     static_assert(FMT != 0 || (RAW16 > NTHR && RAW16 - NTHR <= 64), "slot layout");
     static_assert(FMT == 0 || RAW16 == 2 * NTHR, "slot layout");
     __shared__ Smem<FMT> sm;
@@ -317,7 +334,8 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: keep it scalar
     const int qcol = lane & 31, g = lane >> 5;
-    const int kh = SPLIT ? (wave >> 1) : 0; // SPLIT: this wavefront's key subtile
+    // SPLIT, KEY SPLIT: this wavefront's key subtile
+    const int kh = SPLIT ? (wave >> 1) : KS8 ? (wave >> 2) : 0;
 
     // ---- workgroup -> (sequence, head, query tile).  Workgroups are dispatched round-robin over
     // the 8 XCDs; each XCD gets a contiguous set of heads (their K/V stay in its L2) and within
@@ -351,13 +369,14 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     const int n_tiles = (kv_end_wg + KT - 1) / KT;
 
     // ---- this wavefront's 32-row query blocks: w and 7 - w of the tile (balances the causal
-    // diagonal across wavefronts); SPLIT: block w & 1; NARROW: block w
+    // diagonal across wavefronts); SPLIT: block w & 1; NARROW: block w; KEY SPLIT: as w & 3
     int kv_end_b[NJ], kv_full_b[NJ], qi[NJ], lim[NJ];
     bool q_ok[NJ];
     int64_t row[NJ];
     // first query row of this wavefront's j-th block (wavefront-uniform)
     auto block_q0 = [&](int j) {
-        return q_wg0 + WQ * (SPLIT ? (wave & 1) : NARROW ? wave : (j == 0 ? wave : 7 - wave));
+        return q_wg0 +
+               WQ * (SPLIT ? (wave & 1) : NARROW ? wave : (j == 0 ? (wave & 3) : 7 - (wave & 3)));
     };
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -395,8 +414,24 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     //   Q8_0 (272 pieces per tensor): slot 0 = K piece tid, slot 1 = V piece tid, slot 2 = the
     //   16 remaining K pieces on wavefront 0 and the 16 remaining V pieces on wavefront 1.
     //   FP16 (512 pieces per tensor): slots 0, 1 = K pieces tid, tid + 256; slots 2, 3 = V.
+    //   KEY SPLIT (512 threads): Q8_0 slot 0 = K piece tid on wavefronts 0-3 and V piece
+    //   tid - 256 on 4-7, slot 1 = the 16 remaining K (wavefront 0) and V (wavefront 1) pieces;
+    //   FP16 slot 0 = K piece tid, slot 1 = V piece tid.
     auto slot = [&](int sl, int &tensor, int &piece) -> bool {
-        if constexpr (FMT == 0) {
+        if constexpr (KS8 && FMT == 0) {
+            if (sl == 0) {
+                tensor = wave >> 2;
+                piece = tid & (NTHR - 1);
+                return true;
+            }
+            tensor = wave;
+            piece = NTHR + lane;
+            return wave < 2 && lane < RAW16 - NTHR;
+        } else if constexpr (KS8) {
+            tensor = sl;
+            piece = tid;
+            return true;
+        } else if constexpr (FMT == 0) {
             if (sl < 2) {
                 tensor = sl;
                 piece = tid;
@@ -423,6 +458,20 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     (uint32_t)(uintptr_t)(lds_void *)dst);
                 dma16(tensor ? rv : rk, off, base);
             }
+        }
+    };
+    // raw rows of buffer buf -> operand tile buf; keys from `valid` on lie past the chunk.
+    // KEY SPLIT: K by wavefronts 0-3, V by 4-7 (each part over 256 threads).
+    auto unpack = [&](int buf, int valid) {
+        if constexpr (KS8) {
+            if (wave < 4)
+                unpack_tile<FMT, !CLEAN, 1>(sm.raw[buf][0], sm.raw[buf][1], sm.tile[buf], tid,
+                                            valid);
+            else
+                unpack_tile<FMT, !CLEAN, 2>(sm.raw[buf][0], sm.raw[buf][1], sm.tile[buf],
+                                            tid - NTHR, valid);
+        } else {
+            unpack_tile<FMT, !CLEAN>(sm.raw[buf][0], sm.raw[buf][1], sm.tile[buf], tid, valid);
         }
     };
 
@@ -456,9 +505,9 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 qreg[j][kk] = qrow[2 * kk + g];
-            // SPLIT: only the first key subtile's wavefront resumes from the state; the other
-            // starts empty and is merged in at the end
-            if (!SPLIT || kh == 0)
+            // SPLIT, KEY SPLIT: only the first key subtile's wavefront resumes from the state;
+            // the other starts empty and is merged in at the end
+            if (!KSPLIT || kh == 0)
                 m_old[j] = a.m[row[j]];
         } else {
 #pragma unroll
@@ -466,17 +515,17 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                 qreg[j][kk] = half8{};
         }
     }
-    // Tile 1's copies go last: at least two per thread (slots 0 and 1), so waiting until at
-    // most two vector-memory loads are outstanding (they complete in order) leaves only those
+    // Tile 1's copies go last: at least kTileCopiesMin per thread, so waiting until at most
+    // that many vector-memory loads are outstanding (they complete in order) leaves only those
     // in flight while tile 0 is unpacked; they have landed before the barrier after it.
     if (n_tiles > 1) {
         fetch(1, 1);
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+        __builtin_amdgcn_s_waitcnt(kWaitTile1);
     } else {
         __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
-    unpack_tile<FMT, !CLEAN>(sm.raw[0][0], sm.raw[0][1], sm.tile[0], tid, a.n_kv);
+    unpack(0, a.n_kv);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -543,7 +592,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                 for (int half = 0; half < 2; ++half)
     #pragma unroll
                     for (int si = 0; si < NS; ++si) {
-                        const int sub = SPLIT ? kh : si;
+                        const int sub = KSPLIT ? kh : si;
                         const int krow = (32 * sub + qcol) * KP + 8 * g;
                         if (FMT == 0 && half == 1) {
     #pragma unroll
@@ -569,8 +618,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                         }
                     }
                 // independent VALU work for the matrix instructions above to overlap with
-                unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
-                                 sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
+                unpack((t + 1) & 1, a.n_kv - (t + 1) * KT);
 
                 // u = S*log2(e)/8 - ref, the exponent relative to the reference maximum before
                 // this tile (0 while it is -inf)
@@ -580,7 +628,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     base[j] = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
     #pragma unroll
                 for (int si = 0; si < NS; ++si) {
-                    const int sub = SPLIT ? kh : si;
+                    const int sub = KSPLIT ? kh : si;
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float4 m4 = {kScaleLog2, kScaleLog2, kScaleLog2, kScaleLog2};
@@ -606,7 +654,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                         const int rel = lim[j] - key0 - 4 * g;
     #pragma unroll
                         for (int si = 0; si < NS; ++si) {
-                            const int sub = SPLIT ? kh : si;
+                            const int sub = KSPLIT ? kh : si;
                             if (key0 + 32 * sub + 32 > kv_full_b[j]) {
     #pragma unroll
                                 for (int v = 0; v < 16; ++v)
@@ -684,7 +732,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
                     for (int si = 0; si < NS; ++si)
     #pragma unroll
                         for (int tt = 0; tt < 2; ++tt) {
-                            const int sub = SPLIT ? kh : si;
+                            const int sub = KSPLIT ? kh : si;
                             const int pos = 32 * sub + 16 * tt + 8 * g;
                             const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
                             const half8 a1 =
@@ -699,8 +747,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
         if (key0 < kv_end_w) {
             compute(jlo_c);
         } else {
-            unpack_tile<FMT, !CLEAN>(sm.raw[(t + 1) & 1][0], sm.raw[(t + 1) & 1][1],
-                             sm.tile[(t + 1) & 1], tid, a.n_kv - (t + 1) * KT);
+            unpack((t + 1) & 1, a.n_kv - (t + 1) * KT);
         }
         __builtin_amdgcn_s_waitcnt(0); // raw rows of tile t+2 have landed before the barrier
         __syncthreads();
@@ -728,41 +775,61 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
             tile(t, std::integral_constant<int, 0>{});
     }
 
-    if constexpr (SPLIT) {
-        // merge the two key subtiles' states of each block: the second subtile's wavefront
-        // (kh = 1) leaves its per-lane state in LDS (the loop's last barrier has retired every
-        // use of the tile buffers), the first (kh = 0, same lanes, same block) folds it in
-        static_assert(sizeof(Smem<FMT>) >= 2 * 64 * 36 * sizeof(float), "merge area");
-        float *xb = reinterpret_cast<float *>(&sm) + ((wave & 1) * 64 + lane) * 36;
-        if (kh == 1) {
+    // The key-splitting forms merge the two key subtiles' states of each block: the second
+    // subtile's wavefront (kh = 1) leaves its per-lane state in LDS (the loop's last barrier has
+    // retired every use of the tile buffers), the first (kh = 0, same lanes, same block) folds it
+    // in.
+    auto stash = [&](int j, float *xb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            xb[v] = o[j][0][v];
+            xb[16 + v] = o[j][1][v];
+        }
+        xb[32] = l_part[j];
+        xb[33] = m_ref[j];
+        xb[34] = m_top[j];
+        xb[35] = saw[j] ? 1.f : 0.f;
+    };
+    auto fold = [&](int j, const float *xb) {
+        const float mb = xb[33];
+        if (mb != -INFINITY) { // the other subtile's state is not empty
+            const float ma = m_ref[j];
+            const float mn = fmaxf(ma, mb);
+            const float fa = (ma == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ma - mn);
+            const float fb = __builtin_amdgcn_exp2f(mb - mn);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                xb[v] = o[0][0][v];
-                xb[16 + v] = o[0][1][v];
+                o[j][0][v] = o[j][0][v] * fa + xb[v] * fb;
+                o[j][1][v] = o[j][1][v] * fa + xb[16 + v] * fb;
             }
-            xb[32] = l_part[0];
-            xb[33] = m_ref[0];
-            xb[34] = m_top[0];
-            xb[35] = saw[0] ? 1.f : 0.f;
+            l_part[j] = l_part[j] * fa + xb[32] * fb;
+            m_ref[j] = mn;
         }
+        m_top[j] = fmaxf(m_top[j], xb[34]);
+        saw[j] = saw[j] || xb[35] != 0.f;
+    };
+    if constexpr (SPLIT) {
+        static_assert(sizeof(Smem<FMT>) >= 2 * 64 * 36 * sizeof(float), "merge area");
+        float *xb = reinterpret_cast<float *>(&sm) + ((wave & 1) * 64 + lane) * 36;
+        if (kh == 1)
+            stash(0, xb);
         __syncthreads();
-        if (kh == 0) {
-            const float mb = xb[33];
-            if (mb != -INFINITY) { // the other subtile's state is not empty
-                const float ma = m_ref[0];
-                const float mn = fmaxf(ma, mb);
-                const float fa = (ma == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ma - mn);
-                const float fb = __builtin_amdgcn_exp2f(mb - mn);
+        if (kh == 0)
+            fold(0, xb);
+    }
+    if constexpr (KS8) {
+        // one block at a time; the barrier after each pass retires its reads before the area is
+        // reused (by the next pass, then by the write-back's staging)
+        static_assert(sizeof(Smem<FMT>) >= 4 * 64 * 36 * sizeof(float), "merge area");
+        float *xb = reinterpret_cast<float *>(&sm) + ((wave & 3) * 64 + lane) * 36;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    o[0][0][v] = o[0][0][v] * fa + xb[v] * fb;
-                    o[0][1][v] = o[0][1][v] * fa + xb[16 + v] * fb;
-                }
-                l_part[0] = l_part[0] * fa + xb[32] * fb;
-                m_ref[0] = mn;
-            }
-            m_top[0] = fmaxf(m_top[0], xb[34]);
-            saw[0] = saw[0] || xb[35] != 0.f;
+        for (int j = 0; j < NJ; ++j) {
+            if (kh == 1)
+                stash(j, xb);
+            __syncthreads();
+            if (kh == 0)
+                fold(j, xb);
+            __syncthreads();
         }
     }
 
@@ -782,7 +849,7 @@ __global__ __launch_bounds__(NTHR, 2) void accumulate_kernel(AccumulateArgs a)
     float *stg_flag = stg + WQ * kStagePitch, *stg_l = stg_flag + WQ;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        if (kv_end_b[j] > 0 && (!SPLIT || kh == 0)) { // uniform per wavefront
+        if (kv_end_b[j] > 0 && (!KSPLIT || kh == 0)) { // uniform per wavefront
             const float l_tot = half_swap_sum(l_part[j]);
             const bool wr = q_ok[j] && saw[j];
             const float rr = wr ? __builtin_amdgcn_exp2f(m_ref[j] - m_top[j]) : 0.f;
@@ -987,9 +1054,9 @@ static int workgroup_slots()
 // position kv_pos0 see none, and the kernel maps the first workgroups to the last query tiles, so
 // the grid ends at the first tile that holds a row at or past kv_pos0.
 template <int FMT, bool CLEAN>
-static void launch_form(const AccumulateArgs &a, bool split, bool narrow, hipStream_t s)
+static void launch_form(const AccumulateArgs &a, int form, hipStream_t s)
 {
-    const int rows = split ? QT : narrow ? QT / 2 : QT;
+    const int rows = form == kNarrow ? QT / 2 : QT;
     const int64_t n_qt = (a.M + rows - 1) / rows;
     int64_t first_row = 0;
     if (a.causal && a.kv_pos0 > a.q_pos0)
@@ -997,43 +1064,58 @@ static void launch_form(const AccumulateArgs &a, bool split, bool narrow, hipStr
     if (first_row >= a.M)
         return; // no row sees the chunk
     const dim3 grid((unsigned)((n_qt - first_row / rows) * a.B * a.H));
-    if (split)
-        hipLaunchKernelGGL((accumulate_kernel<FMT, true, false, CLEAN>), grid, dim3(NTHR), 0, s,
+    switch (form) {
+    case kSplit:
+        hipLaunchKernelGGL((accumulate_kernel<FMT, kSplit, CLEAN>), grid, dim3(NTHR), 0, s, a);
+        break;
+    case kNarrow:
+        hipLaunchKernelGGL((accumulate_kernel<FMT, kNarrow, CLEAN>), grid, dim3(NTHR), 0, s, a);
+        break;
+    case kKeySplit:
+        hipLaunchKernelGGL((accumulate_kernel<FMT, kKeySplit, CLEAN>), grid, dim3(2 * NTHR), 0, s,
                            a);
-    else if (narrow)
-        hipLaunchKernelGGL((accumulate_kernel<FMT, false, true, CLEAN>), grid, dim3(NTHR), 0, s,
-                           a);
-    else
-        hipLaunchKernelGGL((accumulate_kernel<FMT, false, false, CLEAN>), grid, dim3(NTHR), 0, s,
-                           a);
+        break;
+    default:
+        hipLaunchKernelGGL((accumulate_kernel<FMT, kWide, CLEAN>), grid, dim3(NTHR), 0, s, a);
+    }
 }
 
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s)
 {
-    // up to 64 query rows (two blocks): split the keys of every tile between wavefront pairs
-    const bool split = a.M <= 2 * WQ;
-    // 128-row workgroups when 256-row ones would not fill the chip's workgroup slots and the
-    // causal diagonal crosses the chunk: the query tiles then see different numbers of keys, the
-    // launch lasts as long as the tile that sees the most, and halving the rows per workgroup
-    // halves that tile's work per key.  Where every row sees the whole chunk the load is even
-    // and the 256-row form, which unpacks each K/V tile for twice the rows, is a little faster.
-    // Q8A_ROWS_PER_WORKGROUP (128 or 256) fixes the choice.
+    // The tile form.  Up to 64 query rows (two blocks): split the keys of every tile between
+    // wavefront pairs.  Otherwise 256-row workgroups, unless they would not fill the chip's
+    // workgroup slots (2 per compute unit):
+    //   * where the causal diagonal crosses the chunk, the query tiles see different numbers of
+    //     keys and the launch lasts as long as the tile that sees the most; 128-row workgroups
+    //     halve that tile's work per key;
+    //   * where every row sees the whole chunk the load is even; with at most one workgroup per
+    //     compute unit, the 8-wavefront key-split form gives every SIMD two wavefronts while
+    //     each K/V tile is still unpacked once for 256 rows.
+    // Q8A_ROWS_PER_WORKGROUP = 128, 256 or 256k (256 rows, keys split over 8 wavefronts) fixes
+    // the form for more than 64 rows.
+    const int slots = workgroup_slots();
     const int64_t wide = (int64_t)((a.M + QT - 1) / QT) * a.B * a.H;
     const bool diagonal = a.causal && a.q_pos0 < a.kv_pos0 + a.n_kv - 1;
-    bool narrow = diagonal && wide < workgroup_slots();
-    if (const char *env = std::getenv("Q8A_ROWS_PER_WORKGROUP")) {
+    int form = kWide;
+    if (a.M <= 2 * WQ)
+        form = kSplit;
+    else if (wide < slots)
+        form = diagonal ? kNarrow : 2 * wide <= slots ? kKeySplit : kWide;
+    const char *env = std::getenv("Q8A_ROWS_PER_WORKGROUP");
+    if (env && form != kSplit) {
         if (std::strcmp(env, "128") == 0)
-            narrow = true;
+            form = kNarrow;
         else if (std::strcmp(env, "256") == 0)
-            narrow = false;
+            form = kWide;
+        else if (std::strcmp(env, "256k") == 0)
+            form = kKeySplit;
     }
-    narrow = narrow && !split;
     if (kv_dtype != 0)
-        launch_form<1, true>(a, split, narrow, s); // FP16 rows: 128 bytes, always clean
+        launch_form<1, true>(a, form, s); // FP16 rows: 128 bytes, always clean
     else if (a.n_kv % 4 == 0)
-        launch_form<0, true>(a, split, narrow, s);
+        launch_form<0, true>(a, form, s);
     else
-        launch_form<0, false>(a, split, narrow, s);
+        launch_form<0, false>(a, form, s);
     return hipGetLastError();
 }
 

@@ -19,10 +19,10 @@ def orc():
     return oracle
 
 
-@pytest.fixture(params=["128", "256"])
+@pytest.fixture(params=["128", "256", "256k"])
 def rows_per_workgroup(request, monkeypatch):
-    """Run with 128 and with 256 query rows per workgroup forced, so both tile forms of the
-    accumulate kernel meet every case (tests without this fixture run the library's own
-    choice)."""
+    """Run with each tile form of the accumulate kernel forced for more than 64 query rows: 128
+    rows per workgroup, 256 rows, and 256 rows with every tile's keys split over 8 wavefronts
+    (tests without this fixture run the library's own choice)."""
     monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", request.param)
     return request.param
