@@ -40,6 +40,7 @@
 //     sequence of 32 heads): 128-row workgroups, one block per wavefront (see NARROW below).
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -581,25 +582,25 @@ void accumulate_kernel(AccumulateArgs a)
                 // si-th key subtile this wavefront covers.  Q8_0: the first block's products (dims
                 // 0-31) are scaled by kr before the second block's are added.
                 floatx16 s[NJ][NS];
-    #pragma unroll
+#pragma unroll
                 for (int j = JLO; j < NJ; ++j)
-    #pragma unroll
+#pragma unroll
                     for (int si = 0; si < NS; ++si)
-    #pragma unroll
+#pragma unroll
                         for (int v = 0; v < 16; ++v)
                             s[j][si][v] = 0.f;
-    #pragma unroll
+#pragma unroll
                 for (int half = 0; half < 2; ++half)
-    #pragma unroll
+#pragma unroll
                     for (int si = 0; si < NS; ++si) {
                         const int sub = KSPLIT ? kh : si;
                         const int krow = (32 * sub + qcol) * KP + 8 * g;
                         if (FMT == 0 && half == 1) {
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const float4 r4 =
-                                    *reinterpret_cast<const float4 *>(&T.kr[32 * sub + 8 * i + 4 * g]);
-    #pragma unroll
+                                const float4 r4 = *reinterpret_cast<const float4 *>(
+                                    &T.kr[32 * sub + 8 * i + 4 * g]);
+#pragma unroll
                                 for (int j = JLO; j < NJ; ++j) {
                                     s[j][si][4 * i + 0] *= r4.x;
                                     s[j][si][4 * i + 1] *= r4.y;
@@ -608,10 +609,10 @@ void accumulate_kernel(AccumulateArgs a)
                                 }
                             }
                         }
-    #pragma unroll
+#pragma unroll
                         for (int kk = 2 * half; kk < 2 * half + 2; ++kk) {
                             const half8 ak = *reinterpret_cast<const half8 *>(&T.k[krow + 16 * kk]);
-    #pragma unroll
+#pragma unroll
                             for (int j = JLO; j < NJ; ++j)
                                 s[j][si] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[j][kk],
                                                                                  s[j][si], 0, 0, 0);
@@ -623,23 +624,24 @@ void accumulate_kernel(AccumulateArgs a)
                 // u = S*log2(e)/8 - ref, the exponent relative to the reference maximum before
                 // this tile (0 while it is -inf)
                 float base[NJ];
-    #pragma unroll
+#pragma unroll
                 for (int j = JLO; j < NJ; ++j)
                     base[j] = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
-    #pragma unroll
+#pragma unroll
                 for (int si = 0; si < NS; ++si) {
                     const int sub = KSPLIT ? kh : si;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float4 m4 = {kScaleLog2, kScaleLog2, kScaleLog2, kScaleLog2};
                         if constexpr (FMT == 0)
                             m4 = *reinterpret_cast<const float4 *>(&T.km[32 * sub + 8 * i + 4 * g]);
-    #pragma unroll
+#pragma unroll
                         for (int j = JLO; j < NJ; ++j) {
-                            s[j][si][4 * i + 0] = __builtin_fmaf(s[j][si][4 * i + 0], m4.x, -base[j]);
-                            s[j][si][4 * i + 1] = __builtin_fmaf(s[j][si][4 * i + 1], m4.y, -base[j]);
-                            s[j][si][4 * i + 2] = __builtin_fmaf(s[j][si][4 * i + 2], m4.z, -base[j]);
-                            s[j][si][4 * i + 3] = __builtin_fmaf(s[j][si][4 * i + 3], m4.w, -base[j]);
+                            const int e = 4 * i;
+                            s[j][si][e + 0] = __builtin_fmaf(s[j][si][e + 0], m4.x, -base[j]);
+                            s[j][si][e + 1] = __builtin_fmaf(s[j][si][e + 1], m4.y, -base[j]);
+                            s[j][si][e + 2] = __builtin_fmaf(s[j][si][e + 2], m4.z, -base[j]);
+                            s[j][si][e + 3] = __builtin_fmaf(s[j][si][e + 3], m4.w, -base[j]);
                         }
                     }
                 }
@@ -648,15 +650,15 @@ void accumulate_kernel(AccumulateArgs a)
                 // ragged chunk end, padding rows) are masked element by element; the common case
                 // skips this with one wavefront-uniform test.
                 if (key0 + KT > kv_full_w) {
-    #pragma unroll
+#pragma unroll
                     for (int j = JLO; j < NJ; ++j) {
                         // key key0 + 32*sub + 8*(v/4) + 4*g + v%4 is visible iff it is <= lim
                         const int rel = lim[j] - key0 - 4 * g;
-    #pragma unroll
+#pragma unroll
                         for (int si = 0; si < NS; ++si) {
                             const int sub = KSPLIT ? kh : si;
                             if (key0 + 32 * sub + 32 > kv_full_b[j]) {
-    #pragma unroll
+#pragma unroll
                                 for (int v = 0; v < 16; ++v)
                                     s[j][si][v] = (32 * sub + 8 * (v >> 2) + (v & 3) <= rel)
                                                       ? s[j][si][v] : -INFINITY;
@@ -667,12 +669,12 @@ void accumulate_kernel(AccumulateArgs a)
                 bool need_any = false;
                 float mx[NJ];
                 bool need[NJ];
-    #pragma unroll
+#pragma unroll
                 for (int j = JLO; j < NJ; ++j) {
                     if constexpr (NS == 2) {
                         float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
                         float mb = vmax3(s[j][1][0], s[j][1][1], s[j][1][2]);
-    #pragma unroll
+#pragma unroll
                         for (int v = 3; v < 15; v += 2) {
                             ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
                             mb = vmax3(mb, s[j][1][v], s[j][1][v + 1]);
@@ -680,7 +682,7 @@ void accumulate_kernel(AccumulateArgs a)
                         mx[j] = vmax3(ma, mb, fmaxf(s[j][0][15], s[j][1][15]));
                     } else {
                         float ma = vmax3(s[j][0][0], s[j][0][1], s[j][0][2]);
-    #pragma unroll
+#pragma unroll
                         for (int v = 3; v < 15; v += 2)
                             ma = vmax3(ma, s[j][0][v], s[j][0][v + 1]);
                         mx[j] = fmaxf(ma, s[j][0][15]);
@@ -694,7 +696,7 @@ void accumulate_kernel(AccumulateArgs a)
                     need_any = need_any || need[j];
                 }
                 if (__builtin_amdgcn_ballot_w64(need_any)) {
-    #pragma unroll
+#pragma unroll
                     for (int j = JLO; j < NJ; ++j) {
                         const float delta = need[j] ? mx[j] : 0.f; // new ref = base + delta
                         const float alpha = (m_ref[j] == -INFINITY)
@@ -704,20 +706,20 @@ void accumulate_kernel(AccumulateArgs a)
                         o[j][1] *= alpha;
                         if (need[j])
                             m_ref[j] = base[j] + delta;
-    #pragma unroll
+#pragma unroll
                         for (int si = 0; si < NS; ++si)
                             s[j][si] -= delta;
                     }
                 }
                 // per query block: P = exp2(u) (l sums the FP32 values), P to FP16, then
                 // O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
-    #pragma unroll
+#pragma unroll
                 for (int j = JLO; j < NJ; ++j) {
                     float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
                     half8 p16[NS][2];
-    #pragma unroll
+#pragma unroll
                     for (int si = 0; si < NS; ++si) {
-    #pragma unroll
+#pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const float p = __builtin_amdgcn_exp2f(s[j][si][v]);
                             s[j][si][v] = p;
@@ -728,13 +730,14 @@ void accumulate_kernel(AccumulateArgs a)
                     }
                     l_part[j] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
                     // the V tile's key order matches the accumulator layout
-    #pragma unroll
+#pragma unroll
                     for (int si = 0; si < NS; ++si)
-    #pragma unroll
+#pragma unroll
                         for (int tt = 0; tt < 2; ++tt) {
                             const int sub = KSPLIT ? kh : si;
                             const int pos = 32 * sub + 16 * tt + 8 * g;
-                            const half8 a0 = *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
+                            const half8 a0 =
+                                *reinterpret_cast<const half8 *>(&T.vt[qcol * VP + pos]);
                             const half8 a1 =
                                 *reinterpret_cast<const half8 *>(&T.vt[(32 + qcol) * VP + pos]);
                             o[j][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, p16[si][tt],
@@ -1085,22 +1088,28 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
     // The tile form.  Up to 64 query rows (two blocks): split the keys of every tile between
     // wavefront pairs.  Otherwise 256-row workgroups, unless they would not fill the chip's
     // workgroup slots (2 per compute unit):
-    //   * where the causal diagonal crosses the chunk, the query tiles see different numbers of
-    //     keys and the launch lasts as long as the tile that sees the most; 128-row workgroups
-    //     halve that tile's work per key;
-    //   * where every row sees the whole chunk the load is even; with at most one workgroup per
-    //     compute unit, the 8-wavefront key-split form gives every SIMD two wavefronts while
-    //     each K/V tile is still unpacked once for 256 rows.
+    //   * where the causal diagonal crosses the chunk so that the first row sees less than half
+    //     of what the last row sees, the query tiles' work is uneven and the launch lasts as
+    //     long as the tile that sees the most; 128-row workgroups halve that tile's work per key;
+    //   * otherwise the load is (nearly) even; with at most one workgroup per compute unit, the
+    //     8-wavefront key-split form gives every SIMD two wavefronts while each K/V tile is
+    //     still unpacked once for 256 rows.
     // Q8A_ROWS_PER_WORKGROUP = 128, 256 or 256k (256 rows, keys split over 8 wavefronts) fixes
     // the form for more than 64 rows.
     const int slots = workgroup_slots();
     const int64_t wide = (int64_t)((a.M + QT - 1) / QT) * a.B * a.H;
-    const bool diagonal = a.causal && a.q_pos0 < a.kv_pos0 + a.n_kv - 1;
+    // keys of the chunk the first and the last query row see (at least one for the first)
+    auto clamp_keys = [&](int64_t n, int64_t lo) {
+        return std::min<int64_t>(std::max(n, lo), a.n_kv);
+    };
+    const int64_t seen_lo = clamp_keys(a.q_pos0 - a.kv_pos0 + 1, 1);
+    const int64_t seen_hi = clamp_keys(a.q_pos0 + a.M - a.kv_pos0, 0);
+    const bool uneven = a.causal && 2 * seen_lo < seen_hi;
     int form = kWide;
     if (a.M <= 2 * WQ)
         form = kSplit;
     else if (wide < slots)
-        form = diagonal ? kNarrow : 2 * wide <= slots ? kKeySplit : kWide;
+        form = uneven ? kNarrow : 2 * wide <= slots ? kKeySplit : kWide;
     const char *env = std::getenv("Q8A_ROWS_PER_WORKGROUP");
     if (env && form != kSplit) {
         if (std::strcmp(env, "128") == 0)
