@@ -108,9 +108,9 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
  * A row that sees no key of the chunk is left bit-for-bit untouched (tiles that lie wholly above
  * the diagonal are skipped, as in "Core Architecture ...", Sec. 5).  Workgroups take 256 query
  * rows unless n_seq*n_heads*ceil(n_q/256) would not fill the device's workgroup slots (two per
- * compute unit): then 128 rows when the causal diagonal crosses the chunk (q_pos0 < kv_pos0 +
- * n_kv - 1), else, with at most one such workgroup per compute unit, 256 rows whose tile keys are
- * split over 8 wavefronts.  For more than 64 rows the environment variable
+ * compute unit): then 128 rows when, with the causal mask, the first query row sees less than
+ * half the chunk keys the last row sees, else, with at most one such workgroup per compute unit,
+ * 256 rows whose tile keys are split over 8 wavefronts.  For more than 64 rows the environment variable
  * Q8A_ROWS_PER_WORKGROUP = 128, 256 or 256k fixes the form; 128 and 256 give the same results bit
  * for bit, 256k (another summation order) the same to rounding.  Each key position must be
  * accumulated exactly once per state; chunk order is free.  Calls on one state must be
