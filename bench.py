@@ -303,9 +303,10 @@ def measure_append(w, qd, kx, vx, kd, vd, m, l, o, out, lse, chunks, steps):
                     "and accumulates from it" % (len(chunks) - 1, n_new)}
 
 
-def build_streamed_cache(w):
-    """Q8_0 K and V of a streamed workload, drawn and packed chunk by chunk (the FP32 cache never
-    exists whole): a device-resident copy [C, 1, H, chunk, 68] and the pinned host copy."""
+def build_streamed_cache(w, layer=0, resident=True):
+    """Q8_0 K and V of a streamed workload (one layer), drawn and packed chunk by chunk (the FP32
+    cache never exists whole): the pinned host copy [C, 1, H, chunk, 68] and, if resident, a
+    device-resident copy (else None)."""
     import torch
 
     import chunked_flashattention_q8_amd as q8a
@@ -316,18 +317,24 @@ def build_streamed_cache(w):
     row = q8a.ROW_BYTES[q8a.KV_Q8_0]
     kh = torch.empty((C, 1, H, chunk, row), dtype=torch.uint8, pin_memory=True)
     vh = torch.empty(kh.shape, dtype=torch.uint8, pin_memory=True)
-    kd = torch.empty(kh.shape, dtype=torch.uint8, device=dev)
+    shape = kh.shape if resident else (1,) + kh.shape[1:]
+    kd = torch.empty(shape, dtype=torch.uint8, device=dev)
     vd = torch.empty_like(kd)
     for c in range(C):
-        k, v = synthetic.gen_kv_chunk(w, c)
+        k, v = synthetic.gen_kv_chunk(w, c, layer)
         n = k.shape[1]
-        q8a.q8_0_pack(torch.from_numpy(k).to(dev), kd[c, 0, :, :n], H * n, w.D)
-        q8a.q8_0_pack(torch.from_numpy(v).to(dev), vd[c, 0, :, :n], H * n, w.D)
-        kh[c].copy_(kd[c])
-        vh[c].copy_(vd[c])
+        i = c if resident else 0
+        # packed dense ([H, n, 68]) and then placed at the chunk's head stride (chunk rows)
+        for src, dst in ((k, kd), (v, vd)):
+            dense = torch.empty((H, n, row), dtype=torch.uint8, device=dev)
+            q8a.q8_0_pack(torch.from_numpy(src).to(dev), dense, H * n, w.D)
+            dst[i, 0, :, :n].copy_(dense)
+        kh[c].copy_(kd[i])
+        vh[c].copy_(vd[i])
         if c % 16 == 15:
-            print("packed chunk %d of %d" % (c + 1, C), file=sys.stderr, flush=True)
-    return kd, vd, kh, vh
+            print("layer %d: packed chunk %d of %d" % (layer, c + 1, C), file=sys.stderr,
+                  flush=True)
+    return (kd, vd, kh, vh) if resident else (None, None, kh, vh)
 
 
 def run_burst(w, steps, warmup, n_split):
@@ -600,6 +607,146 @@ def streamed_line(w, args):
     print(json.dumps(line), flush=True)
 
 
+def build_device_cache(w, layer):
+    """Q8_0 K and V of one layer of a layered workload, packed chunk by chunk into device memory,
+    chunk-major [C, 1, H, chunk, 68] (the FP32 cache never exists whole)."""
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    H, C, chunk = w.H, w.n_chunks, w.chunk
+    row = q8a.ROW_BYTES[q8a.KV_Q8_0]
+    kd = torch.empty((C, 1, H, chunk, row), dtype=torch.uint8, device=dev)
+    vd = torch.empty_like(kd)
+    for c in range(C):
+        k, v = synthetic.gen_kv_chunk(w, c, layer)
+        n = k.shape[1]
+        for src, dst in ((k, kd), (v, vd)):
+            dense = torch.empty((H, n, row), dtype=torch.uint8, device=dev)
+            q8a.q8_0_pack(torch.from_numpy(src).to(dev), dense, H * n, w.D)
+            dst[c, 0, :, :n].copy_(dense)
+    print("layer %d packed" % layer, file=sys.stderr, flush=True)
+    return kd, vd
+
+
+def run_layers(w, steps, warmup):
+    """The layered workload with every layer's cache resident in HBM (16 x 4.56 GB of Q8_0 K and
+    V at 1M tokens fit in the 288 GB of one MI355X): each layer has its own Q, cache, state and
+    output; a step runs every layer in turn: init + its chunk calls (ascending, each writing
+    the final out/lse of the rows it completes; the queries sit at the end of the cache, so the
+    last call completes them all)."""
+    import torch
+
+    import chunked_flashattention_q8_amd as q8a
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    H, chunk, L = w.H, w.chunk, w.layers
+    row = q8a.ROW_BYTES[q8a.KV_Q8_0]
+    if w.q_pos0 + w.M != w.N:
+        raise ValueError("the layered step expects the queries at the end of the cache")
+    caches = [build_device_cache(w, layer) for layer in range(L)]
+    qs = [torch.from_numpy(synthetic.gen_q(w, layer)).view(torch.float16).to(dev)
+          for layer in range(L)]
+    states = [q8a.alloc_state(1, H, w.M, dev) for _ in range(L)]
+    outs = [torch.empty((1, H, w.M, w.D), dtype=torch.float16, device=dev) for _ in range(L)]
+    lses = [torch.empty((1, H, w.M), dtype=torch.float32, device=dev) for _ in range(L)]
+    torch.cuda.synchronize()
+
+    def step():
+        for layer in range(L):
+            m, l, o = states[layer]
+            kd, vd = caches[layer]
+            st = q8a.attn_state_init(m, l, o, 1, H, w.M, w.D, w.q_pos0)
+            for c, (s0, n) in enumerate(w.chunks()):
+                q8a.attn_accumulate_chunk_final(st, qs[layer], kd[c].data_ptr(),
+                                                vd[c].data_ptr(), q8a.KV_Q8_0, s0, n,
+                                                chunk * row, H * chunk * row, outs[layer],
+                                                lses[layer])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    return dict(ms_step=a.elapsed_time(b) / steps, kv_bytes=L * 2 * w.N * H * row,
+                outs=outs, lses=lses)
+
+def layers_parity(w, res, layers):
+    """Oracle check of the layered workload: the sampled rows of the given layers, the oracle
+    fed from its own pack of the same draws."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    threads = oracle.default_threads()
+    rows = synthetic.sample_rows(w)
+    err = []
+    t0 = time.perf_counter()
+    for layer in layers:
+        kb = np.empty((1, w.H, w.N, 68), dtype=np.uint8)
+        vb = np.empty_like(kb)
+        for c, (s0, n) in enumerate(w.chunks()):
+            k, v = synthetic.gen_kv_chunk(w, c, layer)
+            kb[0, :, s0:s0 + n] = oracle.q8_0_pack(k, threads)
+            vb[0, :, s0:s0 + n] = oracle.q8_0_pack(v, threads)
+        prob = oracle.Problem(synthetic.gen_q(w, layer), kb, vb, oracle.KV_Q8_0, w.q_pos0)
+        O_ref, lse_ref = oracle.attention(prob, rows, nthreads=threads)
+        out = res["outs"][layer].float().cpu().numpy().reshape(-1, w.D)[rows]
+        lse = res["lses"][layer].cpu().numpy().reshape(-1)[rows]
+        err.append((out.astype(np.float64) - O_ref, O_ref, lse.astype(np.float64) - lse_ref,
+                    lse_ref))
+        del kb, vb
+    d = np.concatenate([e[0].ravel() for e in err])
+    r = np.concatenate([e[1].ravel() for e in err])
+    dl = np.concatenate([e[2] for e in err])
+    rl = np.concatenate([e[3] for e in err])
+    parity = {"layers_checked": list(layers), "rows_per_layer": int(rows.size),
+              "max_abs": float(np.abs(d).max()),
+              "rel_rms": float(np.sqrt((d ** 2).sum() / (r ** 2).sum())),
+              "lse_rel": float((np.abs(dl) / np.maximum(1, np.abs(rl))).max()),
+              "seconds": round(time.perf_counter() - t0, 1)}
+    parity["ok"] = parity["max_abs"] <= 2e-3 and parity["rel_rms"] <= 1e-3 and \
+        parity["lse_rel"] <= 1e-4
+    return parity
+
+
+def layers_line(w, args):
+    r = run_layers(w, args.steps, args.warmup)
+    flops = w.layers * w.visible_pairs() * 4 * w.D
+    kv = r["kv_bytes"]
+    value = flops / (r["ms_step"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d layers, each B=1 H=%d M=%d N=%d d=64 causal q_pos0=%d "
+                               "with its own Q, Q8_0 K/V cache (all %d resident in HBM, %.1f GB) "
+                               "and state; step = per layer init + %d chunk calls of %d tokens, "
+                               "each writing the final out/lse of the rows it completes" % (
+                                   w.name, w.layers, w.H, w.M, w.N, w.q_pos0, w.layers, kv / 1e9,
+                                   w.n_chunks, w.chunk)},
+        "step_fraction_of_mfma_peak": round(value / PEAK_F16_TFLOPS, 4),
+        "kv_bytes_per_step": kv,
+        "kv_gbps_from_hbm": round(kv / (r["ms_step"] * 1e-3) / 1e9, 3),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["parity_vs_oracle"] = layers_parity(w, r, [0, w.layers - 1])
+    print(json.dumps(line), flush=True)
+
 def secondary_points(main_w, main_res, steps, warmup):
     """The other resident points of the graded shape, each timed like the main step (labelled
     secondary numbers, not the line's value): the same step with plain chunk calls and a
@@ -788,7 +935,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2,
                     help="0-3: resident workloads; 4: the streamed 1M-token workload; "
-                         "5: Mode B burst verification over the 1M-token cache")
+                         "5: Mode B burst verification over the 1M-token cache; 6: the "
+                         "1M-token workload for each of 16 layers")
     ap.add_argument("--chunk", type=int, default=None, help="override B_C")
     ap.add_argument("--feed-dir", default=None,
                     help="workload 4: also feed the cache from files in this directory "
@@ -830,6 +978,9 @@ def main():
     import chunked_flashattention_q8_amd as q8a
 
     w = synthetic.WORKLOADS[args.workload]
+    if w.layers > 1:
+        layers_line(w, args)
+        return
     if w.streamed and not w.causal:
         burst_line(w, args)
         return

@@ -129,7 +129,13 @@ def _stream(stream) -> int | None:
 
 
 def q8_0_pack(x, dst, n_rows: int, row_len: int, stream=None) -> None:
-    """FP32 [n_rows][row_len] -> Q8_0 bytes (n_rows * row_len/32 * 34), on the GPU."""
+    """FP32 [n_rows][row_len] -> Q8_0 bytes (n_rows * row_len/32 * 34), on the GPU.  Both
+    buffers are dense: a tensor view with gaps (e.g. a partial chunk of a strided cache) is
+    refused rather than written past its gaps."""
+    for t in (x, dst):
+        if isinstance(t, torch.Tensor) and not t.is_contiguous():
+            raise ValueError("q8_0_pack takes dense buffers; pack into a contiguous tensor "
+                             "and copy it into the strided view")
     _check(library().q8_0_pack(_ptr(x), _ptr(dst), int(n_rows), int(row_len), _stream(stream)))
 
 

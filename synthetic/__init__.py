@@ -16,11 +16,14 @@ id    name                B   H   M      N          q_pos0     B_C      checked
 3     append_133k         1   32  2048   133120     131072     8192     64/head
 4     stream_1m           1   32  2048   1048576    1046528    16384    32/head
 5     burst_verify_1m     1   32  64     1048576    1048576    16384    all rows
+6     layers16_1m       1   32  2048   1048576    1046528    16384    2/head, 2 layers
 ====  ==================  ==  ==  =====  =========  =========  =======  =========
 
 Workload 5 is Mode B of "Out-of-Core Flash Streaming & Speculative Decode (1M Context)", Sec. 4:
 64 candidate queries (positions just past the cache) attend to the whole 1M-token context with
-no causal mask.
+no causal mask.  Workload 6 is workload 4 for each of 16 layers (the pages' 16-layer model: 16
+caches of 4.56 GB), every layer with its own Q, K, V and state; it is drawn per chunk like the
+streamed workloads and held resident in HBM.
 
 Draws: every tensor is a stack of [rows, 64] slices, one per (sequence, head); slice i of a
 tensor with seed s is filled by ``torch.Tensor.normal_`` (float32, mean 0, std 1) from its own
@@ -30,6 +33,7 @@ the values do not depend on the thread count.  For workload k, Q uses seed ``100
 the method's queries are FP16; K and V stay float32 (they are quantised by the method).  The
 streamed 1M-token workload draws K and V per chunk c with seeds ``1000*k + 100 + 2c`` and
 ``1000*k + 101 + 2c`` and shape [H, B_C, 64], so no process ever holds the whole float32 cache.
+Layer l of a layered workload adds ``100_000 * l`` to each of these seeds (layer 0 keeps them).
 Sampled query rows come from ``numpy.random.default_rng(1000*k + 9)``, drawn per head without
 replacement, always including rows 0 and M - 1.
 """
@@ -58,6 +62,7 @@ class Workload:
     rows_per_head: int | None  # None = every row is checked
     streamed: bool = False
     causal: bool = True
+    layers: int = 1
 
     @property
     def D(self) -> int:
@@ -90,6 +95,8 @@ WORKLOADS = {
     4: Workload(4, "stream_1m", 1, 32, 2048, 1048576, 1046528, 16384, 32, streamed=True),
     5: Workload(5, "burst_verify_1m", 1, 32, 64, 1048576, 1048576, 16384, None, streamed=True,
                 causal=False),
+    6: Workload(6, "layers16_1m", 1, 32, 2048, 1048576, 1046528, 16384, 2, streamed=True,
+                layers=16),
 }
 
 
@@ -130,9 +137,9 @@ def to_f16_bits(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)
 
 
-def gen_q(w: Workload) -> np.ndarray:
+def gen_q(w: Workload, layer: int = 0) -> np.ndarray:
     """Q as FP16 bit patterns, uint16 [B, H, M, 64]."""
-    return to_f16_bits(randn((w.B, w.H, w.M, w.D), 1000 * w.wid + 1))
+    return to_f16_bits(randn((w.B, w.H, w.M, w.D), 1000 * w.wid + 1 + 100_000 * layer))
 
 
 def gen_kv(w: Workload):
@@ -143,12 +150,13 @@ def gen_kv(w: Workload):
     return randn(shape, 1000 * w.wid + 2), randn(shape, 1000 * w.wid + 3)
 
 
-def gen_kv_chunk(w: Workload, c: int):
+def gen_kv_chunk(w: Workload, c: int, layer: int = 0):
     """Float32 K and V of chunk c of a streamed workload, [H, n_kv, 64] each (B = 1)."""
     kv_pos0, n_kv = w.chunks()[c]
     shape = (w.H, n_kv, w.D)
-    return (randn(shape, 1000 * w.wid + 100 + 2 * c),
-            randn(shape, 1000 * w.wid + 101 + 2 * c))
+    base = 1000 * w.wid + 100_000 * layer
+    return (randn(shape, base + 100 + 2 * c),
+            randn(shape, base + 101 + 2 * c))
 
 
 def sample_rows(w: Workload, rows_per_head: int | None = None) -> np.ndarray:

@@ -295,3 +295,14 @@ def test_valid_call_without_device_reports_hip_error():
     rc = lib.q8_0_pack(P(A16), P(A16B), 4, 64, None)
     assert rc == q8a.Q8A_E_HIP
     assert lib.q8a_last_hip_error() != 0
+
+
+def test_binding_refuses_views_with_gaps():
+    """q8_0_pack writes n_rows dense rows: a strided view (a partial chunk of a cache laid out
+    with a larger head stride) is refused by the binding instead of being written past."""
+    cache = torch.zeros((2, 10, 68), dtype=torch.uint8)
+    x = torch.zeros((2, 6, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        q8a.q8_0_pack(x, cache[:, :6], 12, 64)
+    with pytest.raises(ValueError):
+        q8a.q8_0_pack(x.transpose(0, 1), cache, 12, 64)
