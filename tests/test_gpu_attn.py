@@ -93,9 +93,9 @@ def test_row_forms_agree_bit_for_bit(orc, case, monkeypatch):
 
 
 @pytest.mark.parametrize("M", [150, 50])
-def test_fp16_kv_small(orc, M):
+def test_fp16_kv_small(orc, M, rows_per_workgroup):
     B, H, N, q_pos0 = 2, 2, 260, 110
-    say("fp16 kv, M", M)
+    say("fp16 kv, M", M, "rows per workgroup", rows_per_workgroup)
     prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=77, kv_dtype=q8a.KV_F16)
     out, lse, _ = prefill(qd, kd, vd, q8a.KV_F16, B, H, M, N, q_pos0, chunk_list(N, 80))
     O_ref, lse_ref = orc.attention(prob)
