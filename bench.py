@@ -932,7 +932,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the first ~50 steps of a process run slower)")
     ap.add_argument("--workload", type=int, default=2,
                     help="0-3: resident workloads; 4: the streamed 1M-token workload; "
                          "5: Mode B burst verification over the 1M-token cache; 6: the "
