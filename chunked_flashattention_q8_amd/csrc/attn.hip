@@ -29,15 +29,21 @@
 //   * Tiles wholly above the causal diagonal are skipped ("Core Architecture ...", Sec. 5,
 //     causal skipping); rows that see no key of the chunk are not written.
 //   * A state row whose m is -inf is empty: its O and l are not read.  The first two tiles'
-//     copies, Q and m are all in flight together; l and O of resumed rows are loaded right
-//     before the first tile and arrive behind its QK products.  The state rows are written
+//     copies, Q and m are all in flight together (tile 1's copies still in flight while tile 0
+//     is unpacked); l and O of resumed rows are loaded right before the first tile and arrive
+//     behind its QK products.  The state rows are written
 //     back through LDS, four whole rows per store instruction.
 //   * Workgroups are ordered so that each XCD works on a contiguous set of heads (their K/V
 //     stay in that XCD's L2) and the query tiles that see the most keys start first.
 //   * Up to 64 query rows per (sequence, head) (Mode B, decode-like calls): the split-key form,
 //     where the wavefronts split every tile's keys instead of its rows (see SPLIT below).
 //   * Launches whose 256-row workgroups would not fill two slots per compute unit (one
-//     sequence of 32 heads): 128-row workgroups, one block per wavefront (see NARROW below).
+//     sequence of 32 heads): 128-row workgroups, one block per wavefront, where the causal
+//     diagonal makes the chunk uneven (see NARROW below), else 8-wavefront workgroups that
+//     split every tile's keys (see KEY SPLIT below).
+//   * The wavefronts' lower blocks stop seeing keys before their upper blocks on the diagonal;
+//     from then on a tile runs for the upper block alone.  The state and final rows are stored
+//     through the L2 (system scope), not left dirty in it.
 #include <hip/hip_fp16.h>
 
 #include <algorithm>
