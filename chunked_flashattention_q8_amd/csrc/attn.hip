@@ -167,6 +167,14 @@ __device__ __forceinline__ float half_swap_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The final output out = O / l of a row, formed the same way by the finalize kernel and by the
+// accumulate kernel's write-back of the rows a causal chunk completes (so the two agree bit for
+// bit): the reciprocal of l correctly rounded (one IEEE division per row), the product with it
+// in FP32, then one rounding to FP16 (nearest even).  Before that rounding the value is within
+// 1.5 FP32 ulps of O / l.
+__device__ __forceinline__ float final_inv_l(float l) { return 1.0f / l; }
+__device__ __forceinline__ _Float16 final_out(float o, float rl) { return (_Float16)(o * rl); }
+
 template <int FMT> // 0: Q8_0 rows (68 bytes), 1: FP16 rows (128 bytes)
 struct alignas(16) KvTile { // one LDS buffer of unpacked MFMA operands for KT keys
     _Float16 k[KT * KP];                       // K (Q8_0: the int8 values q), [key][dim]
@@ -849,7 +857,7 @@ void accumulate_kernel(AccumulateArgs a)
     // With a.out set, the rows whose query position lies inside the chunk are final (in a
     // causal pass over chunks in ascending key order no later key is visible to them): their
     // out and lse are written as the finalize kernel would from the state just stored (the same
-    // FP32 values, the same division and logarithm), flag 2 instead of 1.
+    // FP32 values, the same reciprocal, product and logarithm), flag 2 instead of 1.
     constexpr int kStagePitch = 68;                                // floats per staged row
     constexpr int kStageFloats = WQ * kStagePitch + 2 * WQ;        // rows, flags, final l
     constexpr int kStageBase = 2 * 64 * 36;                        // floats
@@ -908,20 +916,20 @@ void accumulate_kernel(AccumulateArgs a)
             for (int i = 0; i < WQ / 4; ++i)
                 __builtin_amdgcn_raw_buffer_store_b128(vv[i], rs_o, off[i], 0, kStoreThrough);
             if (fin_block) {
-                // out = O / l rounded once to FP16, 4 values per lane and row
+                // out = O / l as final_out forms it, 4 values per lane and row
                 const __amdgpu_buffer_rsrc_t rs_out =
                     make_rsrc(reinterpret_cast<_Float16 *>(a.out) + head * a.M * kHeadDim,
                               (uint32_t)a.M * (kHeadDim * 2u));
 #pragma unroll
                 for (int i = 0; i < WQ / 4; ++i) {
                     const int r = 4 * i + (lane >> 4), c = lane & 15;
-                    const float lv = stg_l[r];
+                    const float rl = final_inv_l(stg_l[r]);
                     const uint32_t oo =
                         stg_flag[r] == 2.f ? (q0 + r) * (kHeadDim * 2u) + 8u * c : kNoRow;
-                    const half4 h = {(_Float16)(__uint_as_float(vv[i][0]) / lv),
-                                     (_Float16)(__uint_as_float(vv[i][1]) / lv),
-                                     (_Float16)(__uint_as_float(vv[i][2]) / lv),
-                                     (_Float16)(__uint_as_float(vv[i][3]) / lv)};
+                    const half4 h = {final_out(__uint_as_float(vv[i][0]), rl),
+                                     final_out(__uint_as_float(vv[i][1]), rl),
+                                     final_out(__uint_as_float(vv[i][2]), rl),
+                                     final_out(__uint_as_float(vv[i][3]), rl)};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), rs_out,
                                                           oo, 0, kStoreThrough);
                 }
@@ -950,7 +958,7 @@ __global__ __launch_bounds__(256) void state_init_kernel(float *m, float *l, int
     }
 }
 
-// out = O / l rounded once to FP16; lse = m + ln l.  Eight lanes per row, 8 values each.
+// out = O / l (final_inv_l, final_out); lse = m + ln l.  Eight lanes per row, 8 values each.
 __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ m,
                                                        const float *__restrict__ l,
                                                        const float4 *__restrict__ o,
@@ -972,12 +980,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__
             lse[row] = -INFINITY;
     } else {
         const float lv = l[row];
+        const float rl = final_inv_l(lv);
         const float4 x = o[row * 16 + 2 * part];
         const float4 y = o[row * 16 + 2 * part + 1];
-        res[0] = (_Float16)(x.x / lv); res[1] = (_Float16)(x.y / lv);
-        res[2] = (_Float16)(x.z / lv); res[3] = (_Float16)(x.w / lv);
-        res[4] = (_Float16)(y.x / lv); res[5] = (_Float16)(y.y / lv);
-        res[6] = (_Float16)(y.z / lv); res[7] = (_Float16)(y.w / lv);
+        res[0] = final_out(x.x, rl); res[1] = final_out(x.y, rl);
+        res[2] = final_out(x.z, rl); res[3] = final_out(x.w, rl);
+        res[4] = final_out(y.x, rl); res[5] = final_out(y.y, rl);
+        res[6] = final_out(y.z, rl); res[7] = final_out(y.w, rl);
         if (part == 0 && lse)
             lse[row] = mv + logf(lv);
     }

@@ -162,8 +162,10 @@ int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
                       int32_t n_kv, int64_t kv_head_stride, int64_t kv_seq_stride,
                       int32_t causal, void *stream);
 
-/* Final output after the last chunk ("Out-of-Core ...", Sec. 3): out = O / l rounded once to
- * FP16 (nearest even), and lse = m + ln(l) in FP32 (natural log).  Empty rows give out = 0 and
+/* Final output after the last chunk ("Out-of-Core ...", Sec. 3): out = O / l in FP16, formed as
+ * O times the correctly rounded FP32 reciprocal of l, in FP32, rounded once to FP16 (nearest
+ * even; before that rounding within 1.5 FP32 ulps of O / l), and lse = m + ln(l) in FP32
+ * (natural log).  Empty rows give out = 0 and
  * lse = -inf.  out: FP16 [n_seq][n_heads][n_q][64], 16-byte aligned; lse: FP32 [..][n_q] or NULL.
  * The state is not modified. */
 int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream);
