@@ -3,13 +3,16 @@
 
 Prints ONE JSON line on stdout.  A step is one pass of the whole hot path over one batch of
 synthetic input that is already resident in HBM: Q8_0 pack of K and V (FP32 in, 68-byte rows
-out), state init, one attn_accumulate_chunk call per chunk, finalize.  The default workload is
-8 sequences x 32 heads x 2048 causal queries over 2048 keys, head_dim 64, chunks of 512 keys
-(four chunk calls): the M = 2048, 32-head Q8_0 prefill.
+out), the state (described with deferred initialisation: the first chunk call writes every row),
+one attn_accumulate_chunk_final call per chunk (each writes the final out and lse of the rows
+its chunk completes, and not their dead state), so no separate init or finalize launch.  The
+default workload is 8 sequences x 32 heads x 2048 causal queries over 2048 keys, head_dim 64,
+chunks of 512 keys (four chunk calls): the M = 2048, 32-head Q8_0 prefill.
 
 value     = causal attention FLOPs per step (4 * 64 per visible (query, key) pair per head) /
             step time, in TFLOP/s.
-value is timed over --steps steps with no instrumentation inside the timed region.
+value is timed over --steps steps with no instrumentation inside the timed region; a second
+pass records an event at every step boundary and gives the median and minimum step.
 roofline  = the accumulate kernel (the dominant one): algorithmic FLOPs per launch / its mean
             launch duration from HIP events recorded around every launch on the launch stream
             in a second, separately timed pass, against the dense FP16 MFMA peak of MI355X
@@ -94,12 +97,23 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
 
 
-def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, fused=True):
+STEP_FORMS = {
+    "lean": "deferred state init (no launch) + chunk calls writing the final out/lse of the "
+            "rows each completes, without their dead state",
+    "fused": "init launch + chunk calls writing the final rows (their state as well)",
+    "plain": "init launch + plain chunk calls + a finalize launch",
+}
+
+
+def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, form="lean"):
     """Time the resident step of workload w; inputs = (q, k, v) already drawn for w, or None.
-    graph=False skips the captured-graph pass and the append measurement.  fused: the chunk
-    calls write the final output of the rows each completes (attn_accumulate_chunk_final), and
-    attn_finalize runs only if some rows are left (queries past the end of the cache);
-    otherwise plain chunk calls and a finalize launch."""
+    graph=False skips the captured-graph pass and the append measurement.  form (STEP_FORMS):
+    "lean" describes the state with attn_state_init_deferred and Q8A_STATE_FINAL_OUT_ONLY, and
+    its chunk calls (attn_accumulate_chunk_final) write the final output of the rows each
+    completes; "fused" is the same after an attn_state_init launch, keeping the completed rows'
+    state; "plain" is an init launch, attn_accumulate_chunk calls and a finalize launch.  With
+    lean and fused, attn_finalize runs only if some rows are left (queries past the end of the
+    cache)."""
     import numpy as np
     import torch
 
@@ -146,6 +160,8 @@ def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, fus
         else:
             fn()
 
+    fused = form != "plain"
+
     def step(record):
         if kv_dtype == q8a.KV_Q8_0:
             timed("pack", lambda: q8a.q8_0_pack(kvx, kvd, 2 * n_rows, 64), record)
@@ -153,7 +169,11 @@ def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, fus
 
         def init():
             st[0] = q8a.attn_state_init(m, l, o, w.B, w.H, w.M, w.D, w.q_pos0)
-        timed("init", init, record)
+        if form == "lean":
+            st[0] = q8a.attn_state_init_deferred(m, l, o, w.B, w.H, w.M, w.D, w.q_pos0,
+                                                 q8a.STATE_FINAL_OUT_ONLY)
+        else:
+            timed("init", init, record)
         kp, vp = kd.data_ptr(), vd.data_ptr()
         for s, n in chunks:
             if fused:
@@ -181,6 +201,16 @@ def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, fus
     t1.record()
     torch.cuda.synchronize()
     ms_clean = t0.elapsed_time(t1) / steps
+    # the same steps with an event at every step boundary: median and minimum of the steps
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    bounds[0].record()
+    for i in range(steps):
+        step(False)
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps))
+    ms_median = float(np.median(per_step))
+    ms_min = per_step[0]
     # timed region with per-launch events (the roofline numbers come from here)
     for key in ev:
         ev[key].clear()
@@ -197,6 +227,7 @@ def run_resident(w, kv_dtype, chunk, steps, warmup, inputs=None, graph=True, fus
             kern[key] = {"launches_per_step": len(d) // steps, "mean_us": 1e3 * float(np.mean(d))}
     acc_ms = [a.elapsed_time(b) for a, b in ev["accumulate"]]
     res = dict(q=q, out=out, lse=lse, ms_clean=ms_clean, ms_events=ms_events, kernels=kern,
+               ms_median=ms_median, ms_min=ms_min,
                acc_mean_ms=float(np.mean(acc_ms)), acc_flops_mean=float(np.mean(acc_flops)),
                acc_per_chunk_us=[1e3 * float(np.mean(acc_ms[i::len(chunks)]))
                                  for i in range(len(chunks))],
@@ -435,6 +466,8 @@ def burst_line(w, args):
         "split_vs_streamed_output_max_abs": r["split_vs_streamed_max_abs"],
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = sampled_cpu_baseline(w, rows_per_head=16)
     print(json.dumps(line), flush=True)
 
 
@@ -604,6 +637,10 @@ def streamed_line(w, args):
         "file_feed": r["file_feed"],
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        base = sampled_cpu_baseline(w)
+        base["extrapolated_kv_gbps"] = round(kv / base["extrapolated_full_step_s"] / 1e9, 4)
+        line["cpu_baseline"] = base
     print(json.dumps(line), flush=True)
 
 
@@ -745,6 +782,7 @@ def layers_line(w, args):
     }
     if not args.no_cpu_baseline:
         line["parity_vs_oracle"] = layers_parity(w, r, [0, w.layers - 1])
+        line["cpu_baseline"] = sampled_cpu_baseline(w, rows_per_head=32)
     print(json.dumps(line), flush=True)
 
 def secondary_points(main_w, main_res, steps, warmup):
@@ -758,12 +796,14 @@ def secondary_points(main_w, main_res, steps, warmup):
 
     out = {}
     same = (main_res["q"], main_res["k"], main_res["v"])
-    points = [("batch8_m2048_q8_0_bc512_finalize_launch", main_w, q8a.KV_Q8_0, 512, same, False),
-              ("incore_m2048_q8_0_bc512", synthetic.WORKLOADS[1], q8a.KV_Q8_0, 512, None, True),
-              ("batch8_m2048_f16kv_bc512", main_w, q8a.KV_F16, 512, same, True),
-              ("batch8_m2048_q8_0_bc2048", main_w, q8a.KV_Q8_0, 2048, same, True)]
-    for name, w, kv, chunk, inputs, fused in points:
-        r = run_resident(w, kv, chunk, steps, warmup, inputs=inputs, graph=False, fused=fused)
+    points = [("batch8_m2048_q8_0_bc512_init_launch", main_w, q8a.KV_Q8_0, 512, same, "fused"),
+              ("batch8_m2048_q8_0_bc512_finalize_launch", main_w, q8a.KV_Q8_0, 512, same,
+               "plain"),
+              ("incore_m2048_q8_0_bc512", synthetic.WORKLOADS[1], q8a.KV_Q8_0, 512, None, "lean"),
+              ("batch8_m2048_f16kv_bc512", main_w, q8a.KV_F16, 512, same, "lean"),
+              ("batch8_m2048_q8_0_bc2048", main_w, q8a.KV_Q8_0, 2048, same, "lean")]
+    for name, w, kv, chunk, inputs, form in points:
+        r = run_resident(w, kv, chunk, steps, warmup, inputs=inputs, graph=False, form=form)
         flops = w.visible_pairs() * 4 * w.D
         acc = r["acc_flops_mean"] / (r["acc_mean_ms"] * 1e-3) / 1e12
         out[name] = {
@@ -774,15 +814,52 @@ def secondary_points(main_w, main_res, steps, warmup):
             "accumulate_mean_launch_us": round(1e3 * r["acc_mean_ms"], 3),
             "accumulate_frac": round(acc / PEAK_F16_TFLOPS, 4),
             "chunk_calls": len(r["chunks"]),
-            "step": ("pack of K and V (one call) + " if kv == q8a.KV_Q8_0 else "(FP16 KV: no pack) ") +
-                    ("init + chunk calls writing the final rows" if fused else
-                     "init + plain chunk calls + a finalize launch"),
+            "ms_per_step_median": round(r["ms_median"], 5),
+            "step": ("pack of K and V (one call) + " if kv == q8a.KV_Q8_0 else
+                     "(FP16 KV: no pack) ") + STEP_FORMS[form],
         }
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_rate(w, q, k, v, kv_dtype, head=0):
+    """The oracle on one thread: pack of one head's K and V and FP64 attention over all its rows,
+    in TFLOP/s of attention (the pack time included), and the seconds it took."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    b, h = divmod(head, w.H)
+    pos = w.q_pos0 + np.arange(w.M, dtype=np.int64)
+    flops = int(np.minimum(pos + 1, w.N).sum()) * 4 * w.D
+    t0 = time.perf_counter()
+    qh = np.ascontiguousarray(q[b:b + 1, h:h + 1])
+    if kv_dtype == 0:
+        prob = oracle.Problem(qh, oracle.q8_0_pack(k[b:b + 1, h:h + 1], 1),
+                              oracle.q8_0_pack(v[b:b + 1, h:h + 1], 1), oracle.KV_Q8_0, w.q_pos0)
+    else:
+        prob = oracle.Problem(qh, synthetic.to_f16_bits(k[b:b + 1, h:h + 1]),
+                              synthetic.to_f16_bits(v[b:b + 1, h:h + 1]), oracle.KV_F16, w.q_pos0)
+    oracle.attention(prob, nthreads=1)
+    dt = time.perf_counter() - t0
+    return flops / dt / 1e12, dt
+
+
 def cpu_baseline(w, res, kv_dtype, budget_s):
-    """The oracle on whole heads (b, h) in order until ~budget_s of wall time has passed."""
+    """The oracle on whole heads (b, h) in order until ~budget_s of wall time has passed, on
+    every host thread; then one head on one thread."""
     import numpy as np
 
     import oracle
@@ -824,12 +901,77 @@ def cpu_baseline(w, res, kv_dtype, budget_s):
               "lse_rel": float((np.abs(dl) / np.maximum(1, np.abs(rl))).max())}
     parity["ok"] = parity["max_abs"] <= 2e-3 and parity["rel_rms"] <= 1e-3 and \
         parity["lse_rel"] <= 1e-4
+    st_rate, st_s = single_thread_rate(w, q, k, v, kv_dtype)
     base = {"value": head_flops * done / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d (sequence, head) pairs in full (Q8_0 pack of their K and V + "
                       "FP64 single-pass causal attention over all %d rows), %.1f s" % (
-                          done, w.B * w.H, w.M, dt)}
+                          done, w.B * w.H, w.M, dt),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": st_rate, "unit": "TFLOP/s", "seconds": round(st_s, 2),
+                              "sample": "(sequence 0, head 0) in full on one thread"}}
     return base, parity
+
+
+def sampled_cpu_baseline(w, layer=0, heads=(0,), rows_per_head=None):
+    """The oracle on sampled rows of a 1M-token workload: for each sampled head, its K and V are
+    drawn (the same draws, chunk by chunk) and packed by the oracle, then FP64 attention of the
+    head's sampled rows over every visible key, on every host thread; one of those rows is
+    timed again on one thread.  Reported in TFLOP/s of attention over the sampled rows (the pack
+    of the head's cache is timed separately), with the full step's time extrapolated from both
+    rates and labelled as such."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    threads = oracle.default_threads()
+    rows_all = synthetic.sample_rows(w, rows_per_head)
+    q = synthetic.gen_q(w, layer)
+    t_pack = t_attn = 0.0
+    flops = 0
+    n_rows = 0
+    st = None
+    for h in heads:
+        t0 = time.perf_counter()
+        kb = np.empty((1, 1, w.N, 68), dtype=np.uint8)
+        vb = np.empty_like(kb)
+        for c, (s0, n) in enumerate(w.chunks()):
+            k, v = synthetic.gen_kv_chunk_head(w, c, h, layer)
+            kb[0, 0, s0:s0 + n] = oracle.q8_0_pack(k, threads)
+            vb[0, 0, s0:s0 + n] = oracle.q8_0_pack(v, threads)
+        t_pack += time.perf_counter() - t0
+        rows = rows_all[(rows_all >= h * w.M) & (rows_all < (h + 1) * w.M)] - h * w.M
+        prob = oracle.Problem(np.ascontiguousarray(q[:, h:h + 1]), kb, vb, oracle.KV_Q8_0,
+                              w.q_pos0)
+        prob.causal = w.causal
+        pos = w.q_pos0 + rows
+        vis = np.minimum(pos + 1, w.N) if w.causal else np.full(rows.size, w.N)
+        t0 = time.perf_counter()
+        oracle.attention(prob, rows, nthreads=threads)
+        t_attn += time.perf_counter() - t0
+        flops += int(vis.sum()) * 4 * w.D
+        n_rows += rows.size
+        if st is None:
+            t0 = time.perf_counter()
+            oracle.attention(prob, rows[:1], nthreads=1)
+            st = (int(vis[0]) * 4 * w.D, time.perf_counter() - t0)
+        del kb, vb
+    full_flops = w.layers * w.visible_pairs() * 4 * w.D
+    rate = flops / t_attn
+    extrap_s = full_flops / rate + t_pack / len(heads) * w.H * w.layers
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d sampled query rows of head(s) %s%s over all their visible keys (FP64 "
+                      "attention, %.1f s), after the oracle's pack of those heads' K and V "
+                      "(%.1f s)" % (n_rows, list(heads),
+                                    " of layer %d" % layer if w.layers > 1 else "", t_attn,
+                                    t_pack),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": st[0] / st[1] / 1e12, "unit": "TFLOP/s",
+                              "seconds": round(st[1], 2), "sample": "one of those rows"},
+            "extrapolated_full_step_s": round(extrap_s, 1),
+            "extrapolation": "full step = all heads' attention at the sampled rate + every "
+                             "head's pack at the sampled pack time"}
 
 
 def read_summary(path):
@@ -855,20 +997,25 @@ def traffic_per_launch():
     return float(t["hbm_bytes_per_launch"])
 
 
-def algorithmic_bytes(w, chunk, fused=True):
-    """Algorithmic HBM bytes of each chunk call: the chunk's K and V rows (136 B per key per
-    head), Q rows of the queries that see the chunk (128 B), their state read (m; l and O only
-    for rows that are not empty) and written (m, l, O: 264 B); fused, also the final output of
-    the rows whose position lies in the chunk (FP16 out 128 B, lse 4 B)."""
+def algorithmic_bytes(w, chunk, form="lean"):
+    """Algorithmic HBM bytes of each chunk call (chunks in ascending order; STEP_FORMS): the
+    chunk's K and V rows (136 B per key per head); for each query row that sees the chunk its Q
+    row (128 B), its state read (m, 4 B, except in the lean form's first call, whose deferred
+    state is not read; l and O, 260 B, for rows that are not empty) and written (m, l, O:
+    264 B); lean and fused, the final output of the rows whose position lies in the chunk (out
+    128 B, lse 4 B), and lean writes no state for those rows."""
     import numpy as np
     pos = w.q_pos0 + np.arange(w.M, dtype=np.int64)
     out = []
     for s in range(0, w.N, chunk):
         n = min(chunk, w.N - s)
         touched = int((pos >= s).sum())
-        nonempty = int((pos >= s).sum()) if s > 0 else 0  # every row sees key 0 first
-        final = int(((pos >= s) & (pos < s + n)).sum()) if fused else 0
-        per_head = n * 136 + touched * (128 + 4 + 264) + nonempty * 260 + final * 132
+        nonempty = touched if s > 0 else 0  # every row sees key 0 first
+        final = int(((pos >= s) & (pos < s + n)).sum()) if form != "plain" else 0
+        m_read = 0 if (form == "lean" and s == 0) else 4
+        state_written = touched - (final if form == "lean" else 0)
+        per_head = (n * 136 + touched * (128 + m_read) + nonempty * 260 + state_written * 264 +
+                    final * 132)
         out.append(per_head * w.B * w.H)
     return out
 
@@ -1012,10 +1159,11 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "%s: B=%d H=%d M=%d N=%d d=64 causal q_pos0=%d, %s KV, B_C=%d "
-                        "(%d chunk calls); step = pack of K and V (one call) + init + chunk calls, each writing "
-                        "the final out/lse of the rows it completes"
+                        "(%d chunk calls); step = %s%s"
                         % (w.name, w.B, w.H, w.M, w.N, w.q_pos0, args.kv.upper(), chunk,
-                           len(res["chunks"])),
+                           len(res["chunks"]),
+                           "pack of K and V (one call) + " if kv_dtype == q8a.KV_Q8_0 else "",
+                           STEP_FORMS["lean"]),
             "kv_dtype": args.kv, "chunk_tokens": chunk,
         },
         "roofline": {
@@ -1032,6 +1180,8 @@ def main():
         },
         "step_fraction_of_mfma_peak": round(value / PEAK_F16_TFLOPS, 4),
         "kv_gbps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "ms_per_step_median": round(res["ms_median"], 5),
+        "ms_per_step_min": round(res["ms_min"], 5),
         "ms_per_step_with_kernel_events": round(res["ms_events"], 5),
         "hip_graph": {"ms_per_step": round(res["ms_graph"], 5),
                       "value": round(flops_step / (res["ms_graph"] * 1e-3) / 1e12, 3),

@@ -32,10 +32,18 @@ Q8A_E_IO = 6
 KV_Q8_0 = 0
 KV_F16 = 1
 STATE_MAGIC = 0x51384154
+# bits of q8a_state.flags (include/q8attn.h)
+STATE_FRESH = 0x1
+STATE_FINAL_OUT_ONLY = 0x2
+FORM_MASK = 0x30
+FORM_AUTO = 0x00
+FORM_WIDE = 0x10
+FORM_NARROW = 0x20
+FORM_KEY_SPLIT = 0x30
 HEAD_DIM = 64
 ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
 
-EXPORTS = ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk",
+EXPORTS = ("q8_0_pack", "attn_state_init", "attn_state_init_deferred", "attn_accumulate_chunk",
            "attn_accumulate_chunk_final", "attn_append_chunk",
            "attn_finalize",
            "attn_state_merge", "attn_accumulate_stream", "attn_accumulate_file",
@@ -78,6 +86,7 @@ def library() -> ctypes.CDLL:
     SP = ctypes.POINTER(q8a_state)
     lib.q8_0_pack.argtypes = [P, P, i64, i32, P]
     lib.attn_state_init.argtypes = [SP, P, P, P, i32, i32, i32, i32, i64, P]
+    lib.attn_state_init_deferred.argtypes = [SP, P, P, P, i32, i32, i32, i32, i64]
     lib.attn_accumulate_chunk.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P]
     lib.attn_accumulate_chunk_final.argtypes = [SP, P, P, P, i32, i64, i32, i64, i64, i32, P,
                                                 P, P]
@@ -93,7 +102,8 @@ def library() -> ctypes.CDLL:
     lib.q8a_status_string.argtypes = [ctypes.c_int]
     lib.q8a_last_hip_error.restype = ctypes.c_int
     lib.q8a_last_hip_error.argtypes = []
-    for name in ("q8_0_pack", "attn_state_init", "attn_accumulate_chunk", "attn_append_chunk",
+    for name in ("q8_0_pack", "attn_state_init", "attn_state_init_deferred",
+                 "attn_accumulate_chunk", "attn_append_chunk",
                  "attn_finalize", "attn_state_merge", "attn_accumulate_stream",
                  "attn_accumulate_file"):
         getattr(lib, name).restype = ctypes.c_int
@@ -146,6 +156,27 @@ def attn_state_init(m, l, o, n_seq: int, n_heads: int, n_q: int, head_dim: int, 
     _check(library().attn_state_init(ctypes.byref(st), _ptr(m), _ptr(l), _ptr(o), int(n_seq),
                                      int(n_heads), int(n_q), int(head_dim), int(q_pos0),
                                      _stream(stream)))
+    return st
+
+
+def attn_state_init_deferred(m, l, o, n_seq: int, n_heads: int, n_q: int, head_dim: int,
+                             q_pos0: int, flags: int = 0) -> q8a_state:
+    """Describe the state buffers without enqueueing anything (flags = STATE_FRESH): the first
+    call that reads the state initialises it.  `flags` adds further q8a_state.flags bits."""
+    st = q8a_state()
+    _check(library().attn_state_init_deferred(ctypes.byref(st), _ptr(m), _ptr(l), _ptr(o),
+                                              int(n_seq), int(n_heads), int(n_q),
+                                              int(head_dim), int(q_pos0)))
+    st.flags |= int(flags)
+    return st
+
+
+def set_flags(st: q8a_state, flags: int) -> q8a_state:
+    """Set q8a_state.flags bits (STATE_FINAL_OUT_ONLY, a FORM_* tile form) on a descriptor;
+    FORM_* bits replace the tile form already set."""
+    if flags & FORM_MASK:
+        st.flags &= ~FORM_MASK
+    st.flags |= int(flags)
     return st
 
 
@@ -243,6 +274,8 @@ def sub_state(st: q8a_state, s0: int, n: int) -> q8a_state:
     """Descriptor of sequences [s0, s0 + n) of an initialised state (same buffers)."""
     if not (0 <= s0 and n >= 1 and s0 + n <= st.n_seq):
         raise ValueError("sequence range outside the state")
+    if st.flags & STATE_FRESH:
+        raise ValueError("take sub-states of an initialised state, not a deferred one")
     sub = q8a_state()
     ctypes.memmove(ctypes.byref(sub), ctypes.byref(st), ctypes.sizeof(q8a_state))
     rows = s0 * st.n_heads * st.n_q

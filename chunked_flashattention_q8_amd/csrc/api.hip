@@ -34,7 +34,7 @@ int row_bytes(int32_t kv_dtype)
 
 int check_state(const q8a_state *st)
 {
-    if (!st || st->magic != Q8A_STATE_MAGIC)
+    if (!st || st->magic != Q8A_STATE_MAGIC || (st->flags & ~Q8A_STATE_FLAGS_KNOWN))
         return Q8A_E_STATE;
     if (st->head_dim != q8a::kHeadDim || st->n_seq < 1 || st->n_heads < 1 || st->n_q < 1 ||
         !st->m || !st->l || !st->o || st->q_pos0 < 0)
@@ -100,7 +100,86 @@ q8a::AccumulateArgs make_args(const q8a_state *st, const void *q, const void *k,
     a.causal = causal;
     a.out = nullptr;
     a.lse = nullptr;
+    a.final_out_only = 0;
+    a.fresh = 0;
+    switch (st->flags & Q8A_FORM_MASK) {
+    case Q8A_FORM_WIDE: a.form = q8a::kFormWide; break;
+    case Q8A_FORM_NARROW: a.form = q8a::kFormNarrow; break;
+    case Q8A_FORM_KEY_SPLIT: a.form = q8a::kFormKeySplit; break;
+    default: a.form = q8a::kFormAuto;
+    }
     return a;
+}
+
+// A state described by attn_state_init_deferred (Q8A_STATE_FRESH) holds nothing yet.  Before the
+// launch of a chunk that every query row sees, the kernel itself treats every row as empty and
+// writes it (a.fresh); otherwise the initialisation is enqueued here first.
+hipError_t prepare_fresh(const q8a_state *st, q8a::AccumulateArgs &a, hipStream_t s)
+{
+    if (!(st->flags & Q8A_STATE_FRESH))
+        return hipSuccess;
+    if (!a.causal || st->q_pos0 >= a.kv_pos0) {
+        a.fresh = 1;
+        return hipSuccess;
+    }
+    return q8a::launch_state_init(st->m, st->l, state_rows(st), s);
+}
+
+// Before a call that reads the state as it stands (finalize, merge): initialise a fresh state.
+hipError_t settle_fresh(q8a_state *st, hipStream_t s)
+{
+    if (!(st->flags & Q8A_STATE_FRESH))
+        return hipSuccess;
+    hipError_t e = q8a::launch_state_init(st->m, st->l, state_rows(st), s);
+    if (e == hipSuccess)
+        st->flags &= ~Q8A_STATE_FRESH;
+    return e;
+}
+
+// Enqueue one accumulate launch (plus the initialisation a fresh state may still owe); clears
+// Q8A_STATE_FRESH once enqueued.
+hipError_t accumulate(q8a_state *st, q8a::AccumulateArgs &a, int kv_dtype, hipStream_t s)
+{
+    hipError_t e = prepare_fresh(st, a, s);
+    if (e == hipSuccess)
+        e = q8a::launch_accumulate(a, kv_dtype, s);
+    if (e == hipSuccess)
+        st->flags &= ~Q8A_STATE_FRESH;
+    return e;
+}
+
+// The arguments of attn_state_init and attn_state_init_deferred.
+int check_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq, int32_t n_heads,
+               int32_t n_q, int32_t head_dim, int64_t q_pos0)
+{
+    if (!st || !m || !l || !o || n_seq < 1 || n_heads < 1 || n_q < 1 || q_pos0 < 0)
+        return Q8A_E_INVAL;
+    if (head_dim != q8a::kHeadDim)
+        return Q8A_E_UNSUPPORTED;
+    // launches stay below 2^32 work-items: 8 lanes per state row in finalize and merge, one
+    // 256-thread workgroup per 256 rows of each (sequence, head) in accumulate
+    if (n_heads > 65535 || n_seq > 65535 || n_q > kMaxRows ||
+        (int64_t)n_seq * n_heads > ((int64_t)1 << 23) ||
+        (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 28))
+        return Q8A_E_UNSUPPORTED;
+    if (!aligned(m, 4) || !aligned(l, 4) || !aligned(o, 16))
+        return Q8A_E_ALIGN;
+    return Q8A_OK;
+}
+
+void describe(q8a_state *st, float *m, float *l, float *o, int32_t n_seq, int32_t n_heads,
+              int32_t n_q, int32_t head_dim, int64_t q_pos0, uint32_t flags)
+{
+    st->m = m;
+    st->l = l;
+    st->o = o;
+    st->n_seq = n_seq;
+    st->n_heads = n_heads;
+    st->n_q = n_q;
+    st->head_dim = head_dim;
+    st->q_pos0 = q_pos0;
+    st->magic = Q8A_STATE_MAGIC;
+    st->flags = flags;
 }
 
 } // namespace
@@ -145,36 +224,28 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
                     int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0,
                     void *stream)
 {
-    if (!st || !m || !l || !o || n_seq < 1 || n_heads < 1 || n_q < 1 || q_pos0 < 0)
-        return Q8A_E_INVAL;
-    if (head_dim != q8a::kHeadDim)
-        return Q8A_E_UNSUPPORTED;
-    // launches stay below 2^32 work-items: 8 lanes per state row in finalize and merge, one
-    // 256-thread workgroup per 256 rows of each (sequence, head) in accumulate
-    if (n_heads > 65535 || n_seq > 65535 || n_q > kMaxRows ||
-        (int64_t)n_seq * n_heads > ((int64_t)1 << 23) ||
-        (int64_t)n_seq * n_heads * n_q > ((int64_t)1 << 28))
-        return Q8A_E_UNSUPPORTED;
-    if (!aligned(m, 4) || !aligned(l, 4) || !aligned(o, 16))
-        return Q8A_E_ALIGN;
+    int rc = check_init(st, m, l, o, n_seq, n_heads, n_q, head_dim, q_pos0);
+    if (rc)
+        return rc;
     const int64_t rows = (int64_t)n_seq * n_heads * n_q;
     hipError_t e = q8a::launch_state_init(m, l, rows, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_failure(e);
-    st->m = m;
-    st->l = l;
-    st->o = o;
-    st->n_seq = n_seq;
-    st->n_heads = n_heads;
-    st->n_q = n_q;
-    st->head_dim = head_dim;
-    st->q_pos0 = q_pos0;
-    st->magic = Q8A_STATE_MAGIC;
-    st->flags = 0;
+    describe(st, m, l, o, n_seq, n_heads, n_q, head_dim, q_pos0, 0);
     return Q8A_OK;
 }
 
-int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, const void *v,
+int attn_state_init_deferred(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
+                             int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0)
+{
+    int rc = check_init(st, m, l, o, n_seq, n_heads, n_q, head_dim, q_pos0);
+    if (rc)
+        return rc;
+    describe(st, m, l, o, n_seq, n_heads, n_q, head_dim, q_pos0, Q8A_STATE_FRESH);
+    return Q8A_OK;
+}
+
+int attn_accumulate_chunk(q8a_state *st, const void *q, const void *k, const void *v,
                           int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
                           int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
                           void *stream)
@@ -185,11 +256,11 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
         return rc;
     q8a::AccumulateArgs a =
         make_args(st, q, k, v, kv_pos0, n_kv, kv_head_stride, kv_seq_stride, causal);
-    hipError_t e = q8a::launch_accumulate(a, kv_dtype, static_cast<hipStream_t>(stream));
+    hipError_t e = accumulate(st, a, kv_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
-int attn_accumulate_chunk_final(const q8a_state *st, const void *q, const void *k,
+int attn_accumulate_chunk_final(q8a_state *st, const void *q, const void *k,
                                 const void *v, int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
                                 int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
                                 void *out, float *lse, void *stream)
@@ -224,11 +295,12 @@ int attn_accumulate_chunk_final(const q8a_state *st, const void *q, const void *
         make_args(st, q, k, v, kv_pos0, n_kv, kv_head_stride, kv_seq_stride, causal);
     a.out = out;
     a.lse = lse;
-    hipError_t e = q8a::launch_accumulate(a, kv_dtype, static_cast<hipStream_t>(stream));
+    a.final_out_only = (st->flags & Q8A_STATE_FINAL_OUT_ONLY) ? 1 : 0;
+    hipError_t e = accumulate(st, a, kv_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
-int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
+int attn_append_chunk(q8a_state *st, const void *q, const float *k_new,
                       const float *v_new, void *k_cache, void *v_cache, int64_t kv_pos0,
                       int32_t n_kv, int64_t kv_head_stride, int64_t kv_seq_stride,
                       int32_t causal, void *stream)
@@ -282,11 +354,11 @@ int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
         return hip_failure(e);
     q8a::AccumulateArgs a = make_args(st, q, k_cache, v_cache, kv_pos0, n_kv, kv_head_stride,
                                       kv_seq_stride, causal);
-    e = q8a::launch_accumulate(a, Q8A_KV_Q8_0, s);
+    e = accumulate(st, a, Q8A_KV_Q8_0, s);
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
-int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream)
+int attn_finalize(q8a_state *st, void *out, float *lse, void *stream)
 {
     int rc = check_state(st);
     if (rc)
@@ -295,12 +367,14 @@ int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream)
         return Q8A_E_INVAL;
     if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
         return Q8A_E_ALIGN;
-    hipError_t e = q8a::launch_finalize(st->m, st->l, st->o, out, lse, state_rows(st),
-                                        static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = settle_fresh(st, s);
+    if (e == hipSuccess)
+        e = q8a::launch_finalize(st->m, st->l, st->o, out, lse, state_rows(st), s);
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
-int attn_state_merge(const q8a_state *dst, const q8a_state *src, void *stream)
+int attn_state_merge(q8a_state *dst, const q8a_state *src, void *stream)
 {
     int rc = check_state(dst);
     if (rc)
@@ -324,12 +398,16 @@ int attn_state_merge(const q8a_state *dst, const q8a_state *src, void *stream)
         for (int j = 0; j < 3; ++j)
             if (overlap(dm[i], bytes[i], sm[j], bytes[j]))
                 return Q8A_E_INVAL;
-    hipError_t e = q8a::launch_merge(dst->m, dst->l, dst->o, src->m, src->l, src->o, rows,
-                                     static_cast<hipStream_t>(stream));
+    if (src->flags & Q8A_STATE_FRESH)
+        return Q8A_OK; // src holds no key: nothing to merge
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = settle_fresh(dst, s);
+    if (e == hipSuccess)
+        e = q8a::launch_merge(dst->m, dst->l, dst->o, src->m, src->l, src->o, rows, s);
     return e == hipSuccess ? Q8A_OK : hip_failure(e);
 }
 
-int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_host,
+int attn_accumulate_stream(q8a_state *st, const void *q, const void *k_host,
                            const void *v_host, int32_t kv_dtype, int64_t n_kv_total,
                            int32_t chunk_tokens, void *const slot_k[2], void *const slot_v[2],
                            int32_t causal, void *compute_stream, void *copy_stream)
@@ -400,7 +478,7 @@ int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_hos
         if (e == hipSuccess) {
             q8a::AccumulateArgs a = make_args(st, q, slot_k[s], slot_v[s], kv_pos0, n_kv,
                                               head_stride, seq_stride, causal);
-            e = q8a::launch_accumulate(a, kv_dtype, cs);
+            e = accumulate(st, a, kv_dtype, cs);
         }
         if (e == hipSuccess)
             e = hipEventRecord(ev_free[s], cs);
@@ -437,7 +515,7 @@ bool read_aligned(int fd, uint8_t *buf, int64_t off, int64_t len)
 
 } // namespace
 
-int attn_accumulate_file(const q8a_state *st, const void *q, int fd_k, int fd_v,
+int attn_accumulate_file(q8a_state *st, const void *q, int fd_k, int fd_v,
                          int64_t file_offset, int32_t kv_dtype, int64_t n_kv_total,
                          int32_t chunk_tokens, void *const ring_k[2], void *const ring_v[2],
                          int64_t ring_bytes, void *const slot_k[2], void *const slot_v[2],
@@ -557,7 +635,7 @@ int attn_accumulate_file(const q8a_state *st, const void *q, int fd_k, int fd_v,
         if (e == hipSuccess) {
             q8a::AccumulateArgs a = make_args(st, q, slot_k[s], slot_v[s], kv_pos0, n_kv,
                                               head_stride, seq_stride, causal);
-            e = q8a::launch_accumulate(a, kv_dtype, cs);
+            e = accumulate(st, a, kv_dtype, cs);
         }
         if (e == hipSuccess)
             e = hipEventRecord(ev_free[s], cs);

@@ -48,8 +48,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "q8attn_internal.h"
@@ -214,11 +212,18 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             const int off = 34 * blk + 2 + 16 * hh, sh = off & 3;
             const uint32_t *p = reinterpret_cast<const uint32_t *>(rr + (off & ~3));
             const uint32_t x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3], x4 = p[4];
+            const float d0 = (float)*reinterpret_cast<const _Float16 *>(rr);
+            const float d1 = (float)*reinterpret_cast<const _Float16 *>(rr + 34);
+            // A block whose scale is 0 contributes 0 whatever its int8 values (q * 0).  The
+            // second block's products are added unscaled (S0 * kr + S1), so its int8 values are
+            // taken as 0 here; the first block needs nothing, its products are multiplied by
+            // kr = d0 / d1 = 0 (or by d0 = 0 when both scales are 0).
+            const uint32_t zk = (blk == 1 && d1 == 0.f) ? 0u : 0xFFFFFFFFu;
             uint32_t w[4];
-            w[0] = __builtin_amdgcn_alignbyte(x1, x0, sh);
-            w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh);
-            w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh);
-            w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh);
+            w[0] = __builtin_amdgcn_alignbyte(x1, x0, sh) & zk;
+            w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh) & zk;
+            w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh) & zk;
+            w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh) & zk;
             half8 q8[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -233,8 +238,6 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             // the key's two logit scales, computed by its 4 lanes alike (lanes qq = 0, 2 store kr
             // and 1, 3 km, the same values twice: no branch); keys past the chunk end get 0
             // (their raw bytes may be anything; they are masked)
-            const float d0 = (float)*reinterpret_cast<const _Float16 *>(rr);
-            const float d1 = (float)*reinterpret_cast<const _Float16 *>(rr + 34);
             const float den = d1 != 0.f ? d1 : 1.f;
             // d0 / den: reciprocal, product and one residual correction (within an ulp or so;
             // no branchy IEEE division sequence in the tile loop)
@@ -522,7 +525,7 @@ void accumulate_kernel(AccumulateArgs a)
                 qreg[j][kk] = qrow[2 * kk + g];
             // SPLIT, KEY SPLIT: only the first key subtile's wavefront resumes from the state;
             // the other starts empty and is merged in at the end
-            if (!KSPLIT || kh == 0)
+            if ((!KSPLIT || kh == 0) && !a.fresh)
                 m_old[j] = a.m[row[j]];
         } else {
 #pragma unroll
@@ -872,6 +875,9 @@ void accumulate_kernel(AccumulateArgs a)
             const float rr = wr ? __builtin_amdgcn_exp2f(m_ref[j] - m_top[j]) : 0.f;
             const int64_t pos = a.q_pos0 + qi[j]; // this lane's query position
             const bool fin = a.out && wr && pos >= a.kv_pos0 && pos < a.kv_pos0 + a.n_kv;
+            // m and l are stored for the rows that saw a key (a fresh state: for every row,
+            // m = -inf and l = 0 where none was seen), except final rows whose state is dead
+            const bool st_ml = q_ok[j] && (saw[j] || a.fresh) && !(fin && a.final_out_only);
             // does the block hold a final row (wavefront-uniform)?
             const int64_t p0 = a.q_pos0 + block_q0(j);
             const bool fin_block = a.out && p0 + WQ > a.kv_pos0 && p0 < a.kv_pos0 + a.n_kv;
@@ -888,11 +894,13 @@ void accumulate_kernel(AccumulateArgs a)
             // are dropped
             const uint32_t q0 = (uint32_t)block_q0(j);
             const float m_st = m_top[j] * kLn2, l_st = l_tot * rr; // the stored m and l
+            // row flags: 0 nothing, 1 the state, 2 the state and the final output, 3 the final
+            // output alone
             if (g == 0) {
-                stg_flag[qcol] = wr ? (fin ? 2.f : 1.f) : 0.f;
+                stg_flag[qcol] = wr ? (fin ? (a.final_out_only ? 3.f : 2.f) : 1.f) : 0.f;
                 stg_l[qcol] = l_st;
             }
-            const uint32_t ml_off = (wr && g == 0) ? (q0 + qcol) * 4u : kNoRow;
+            const uint32_t ml_off = (st_ml && g == 0) ? (q0 + qcol) * 4u : kNoRow;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_st), rs_m, ml_off, 0,
                                                   kStoreThrough);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_st), rs_l, ml_off, 0,
@@ -910,7 +918,8 @@ void accumulate_kernel(AccumulateArgs a)
             for (int i = 0; i < WQ / 4; ++i) {
                 const int r = 4 * i + (lane >> 4), c = lane & 15;
                 vv[i] = *reinterpret_cast<const u32x4 *>(&stg[r * kStagePitch + 4 * c]);
-                off[i] = stg_flag[r] != 0.f ? (q0 + r) * (kHeadDim * 4u) + 16u * c : kNoRow;
+                const float fl = stg_flag[r];
+                off[i] = (fl == 1.f || fl == 2.f) ? (q0 + r) * (kHeadDim * 4u) + 16u * c : kNoRow;
             }
 #pragma unroll
             for (int i = 0; i < WQ / 4; ++i)
@@ -925,7 +934,7 @@ void accumulate_kernel(AccumulateArgs a)
                     const int r = 4 * i + (lane >> 4), c = lane & 15;
                     const float rl = final_inv_l(stg_l[r]);
                     const uint32_t oo =
-                        stg_flag[r] == 2.f ? (q0 + r) * (kHeadDim * 2u) + 8u * c : kNoRow;
+                        stg_flag[r] >= 2.f ? (q0 + r) * (kHeadDim * 2u) + 8u * c : kNoRow;
                     const half4 h = {final_out(__uint_as_float(vv[i][0]), rl),
                                      final_out(__uint_as_float(vv[i][1]), rl),
                                      final_out(__uint_as_float(vv[i][2]), rl),
@@ -1109,8 +1118,7 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
     //   * otherwise the load is (nearly) even; with at most one workgroup per compute unit, the
     //     8-wavefront key-split form gives every SIMD two wavefronts while each K/V tile is
     //     still unpacked once for 256 rows.
-    // Q8A_ROWS_PER_WORKGROUP = 128, 256 or 256k (256 rows, keys split over 8 wavefronts) fixes
-    // the form for more than 64 rows.
+    // a.form, when set, fixes the form for more than 64 rows.
     const int slots = workgroup_slots();
     const int64_t wide = (int64_t)((a.M + QT - 1) / QT) * a.B * a.H;
     // keys of the chunk the first and the last query row see (at least one for the first)
@@ -1125,13 +1133,12 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
         form = kSplit;
     else if (wide < slots)
         form = uneven ? kNarrow : 2 * wide <= slots ? kKeySplit : kWide;
-    const char *env = std::getenv("Q8A_ROWS_PER_WORKGROUP");
-    if (env && form != kSplit) {
-        if (std::strcmp(env, "128") == 0)
+    if (form != kSplit) {
+        if (a.form == kFormNarrow)
             form = kNarrow;
-        else if (std::strcmp(env, "256") == 0)
+        else if (a.form == kFormWide)
             form = kWide;
-        else if (std::strcmp(env, "256k") == 0)
+        else if (a.form == kFormKeySplit)
             form = kKeySplit;
     }
     if (kv_dtype != 0)

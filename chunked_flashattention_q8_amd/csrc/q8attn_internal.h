@@ -28,7 +28,17 @@ struct AccumulateArgs {
     // (null: none); out FP16 [B][H][M][64], lse FP32 [B][H][M] or null
     void *out;
     float *lse;
+    // 1: those rows get out/lse only, their m/l/O are not written
+    int32_t final_out_only;
+    // 1: the state holds nothing yet and every row sees a key of this chunk: no state is read,
+    // and every row is written (rows that saw no key as empty)
+    int32_t fresh;
+    // tile form for more than 64 query rows: kFormAuto (the library's choice) or one forced
+    int32_t form;
 };
+
+// forced tile forms of the accumulate kernel (AccumulateArgs::form)
+constexpr int kFormAuto = 0, kFormWide = 1, kFormNarrow = 2, kFormKeySplit = 3;
 
 hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s);
 // K and V rows [n_seq][n_heads][n_rows][64] FP32 -> Q8_0 rows at k_dst / v_dst + b * seq_stride

@@ -53,12 +53,14 @@ typedef enum {
 
 #define Q8A_STATE_MAGIC 0x51384154u /* "Q8AT" */
 
-/* Host-side descriptor of a caller-owned online-softmax state.  Filled by attn_state_init; the
- * other calls only read it.  A state row whose m is -inf is EMPTY: it has seen no key, its l is 0
- * and its O is treated as zero and never read (so O need not be cleared).
+/* Host-side descriptor of a caller-owned online-softmax state.  Filled by attn_state_init (or
+ * attn_state_init_deferred); the other calls only read it, except that they clear
+ * Q8A_STATE_FRESH.  A state row whose m is -inf is EMPTY: it has seen no key, its l is 0 and its
+ * O is treated as zero and never read (so O need not be cleared).
  * A descriptor of sequences [s0, s0 + n) of an initialised state is a copy of its descriptor
  * with m and l advanced by s0*n_heads*n_q floats, o by 64 times that, and n_seq = n; it may be
- * passed wherever a state is (for example to merge sequence blocks of one state). */
+ * passed wherever a state is (for example to merge sequence blocks of one state).  Take such
+ * copies only of a descriptor without Q8A_STATE_FRESH (each copy would initialise on its own). */
 typedef struct {
     float *m;          /* [n_seq][n_heads][n_q]      running maximum of the scaled logits  */
     float *l;          /* [n_seq][n_heads][n_q]      running sum of e^(S - m)             */
@@ -66,8 +68,37 @@ typedef struct {
     int32_t n_seq, n_heads, n_q, head_dim;
     int64_t q_pos0;    /* absolute position of query row 0 (same for every sequence) */
     uint32_t magic;    /* Q8A_STATE_MAGIC once initialised */
-    uint32_t flags;    /* reserved, 0 */
+    uint32_t flags;    /* Q8A_STATE_* and Q8A_FORM_* bits below; other bits must be 0 */
 } q8a_state;
+
+/* Bits of q8a_state.flags.
+ *
+ * Q8A_STATE_FRESH: the device buffers hold nothing yet.  Set by attn_state_init_deferred, which
+ *   enqueues no work; the first call that reads the state then treats every row as empty and
+ *   writes it.  An accumulate call (any attn_accumulate_* or attn_append_chunk) whose first
+ *   chunk is seen by every query row (causal = 0, or q_pos0 >= the chunk's kv_pos0; for the
+ *   streamed calls the first chunk starts at position 0) writes every row itself in that
+ *   chunk's launch and reads nothing of the old state; any other call first enqueues the same
+ *   initialisation attn_state_init does.  The call clears the bit in the caller's descriptor
+ *   once that work is enqueued; on an error return before it the bit is left set.  A merge
+ *   with a FRESH src has nothing to merge and enqueues nothing.
+ * Q8A_STATE_FINAL_OUT_ONLY: attn_accumulate_chunk_final writes the out and lse of the rows a
+ *   call completes and NOT their m, l and O, which keep what they held before the call (a
+ *   completed row of a causal pass in ascending key order sees no later key, so its state is
+ *   dead).  Everything else, and every other call, is unchanged.  After such a pass, the
+ *   completed rows' state must not be finalised, merged or accumulated further.
+ * Q8A_FORM_*: the accumulate kernel's tile form for states of more than 64 query rows, for
+ *   tuning and tests (Q8A_FORM_AUTO, 0, lets the library choose; see attn_accumulate_chunk).
+ *   WIDE and NARROW give the same results bit for bit; KEY_SPLIT sums in another order and agrees
+ *   with them to rounding. */
+#define Q8A_STATE_FRESH 0x1u
+#define Q8A_STATE_FINAL_OUT_ONLY 0x2u
+#define Q8A_FORM_MASK 0x30u
+#define Q8A_FORM_AUTO 0x00u      /* the library's choice */
+#define Q8A_FORM_WIDE 0x10u      /* 256 query rows per workgroup, 4 wavefronts */
+#define Q8A_FORM_NARROW 0x20u    /* 128 query rows per workgroup, 4 wavefronts */
+#define Q8A_FORM_KEY_SPLIT 0x30u /* 256 query rows, 8 wavefronts splitting each tile's keys */
+#define Q8A_STATE_FLAGS_KNOWN (Q8A_STATE_FRESH | Q8A_STATE_FINAL_OUT_ONLY | Q8A_FORM_MASK)
 
 /* Q8_0 pack ("Core Architecture & The 4-Brick Pipeline", Sec. 5, block_q8_0; row size from
  * "Out-of-Core Flash Streaming ...", Sec. 1).
@@ -92,6 +123,15 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
                     int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0,
                     void *stream);
 
+/* attn_state_init with the device writes deferred: checks the same arguments and fills the same
+ * descriptor, with flags = Q8A_STATE_FRESH, and enqueues nothing (no stream argument).  The
+ * first call on the state initialises the rows (see Q8A_STATE_FRESH); a causal prefill whose
+ * first chunk starts at or before the first query position (as in a prefill from key 0) then
+ * needs no initialisation launch at all.  The initial state is the one of "Out-of-Core ...",
+ * Sec. 3 before its first chunk: every row empty (m = -inf, l = 0). */
+int attn_state_init_deferred(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
+                             int32_t n_heads, int32_t n_q, int32_t head_dim, int64_t q_pos0);
+
 /* Accumulate one KV chunk into the state (the recurrence of "Out-of-Core Flash Streaming ...",
  * Sec. 3, steps 1-6).
  *   q        FP16 [n_seq][n_heads][n_q][64], 16-byte aligned (same Q on every call).
@@ -110,12 +150,11 @@ int attn_state_init(q8a_state *st, float *m, float *l, float *o, int32_t n_seq,
  * rows unless n_seq*n_heads*ceil(n_q/256) would not fill the device's workgroup slots (two per
  * compute unit): then 128 rows when, with the causal mask, the first query row sees less than
  * half the chunk keys the last row sees, else, with at most one such workgroup per compute unit,
- * 256 rows whose tile keys are split over 8 wavefronts.  For more than 64 rows the environment variable
- * Q8A_ROWS_PER_WORKGROUP = 128, 256 or 256k fixes the form; 128 and 256 give the same results bit
- * for bit, 256k (another summation order) the same to rounding.  Each key position must be
- * accumulated exactly once per state; chunk order is free.  Calls on one state must be
- * stream-ordered; calls on different states are independent. */
-int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, const void *v,
+ * 256 rows whose tile keys are split over 8 wavefronts.  For more than 64 rows the Q8A_FORM_*
+ * bits of st->flags fix the form instead.  Each key position must be accumulated exactly once
+ * per state; chunk order is free.  Calls on one state must be stream-ordered; calls on different
+ * states are independent.  st is written only to clear Q8A_STATE_FRESH. */
+int attn_accumulate_chunk(q8a_state *st, const void *q, const void *k, const void *v,
                           int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
                           int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
                           void *stream);
@@ -127,14 +166,15 @@ int attn_accumulate_chunk(const q8a_state *st, const void *q, const void *k, con
  * kv_pos0 + n_kv) sees no key of any later chunk: its out and lse are written as attn_finalize
  * would write them from the state after this call, bit for bit.  Other rows' out and lse are
  * not touched, and the state is updated exactly as by attn_accumulate_chunk (so attn_finalize
- * still works afterwards).  The caller guarantees the order: every key before kv_pos0 that such
- * a row sees must already be in the state.
+ * still works afterwards) -- unless st->flags holds Q8A_STATE_FINAL_OUT_ONLY: then the completed
+ * rows' m, l and O are not written (their state is dead in such a pass).  The caller guarantees
+ * the order: every key before kv_pos0 that such a row sees must already be in the state.
  *   causal   must be 1 (Q8A_E_INVAL otherwise).
  *   out      FP16 [n_seq][n_heads][n_q][64], 16-byte aligned;  lse  FP32 [..][n_q], 4-byte
  *            aligned, or NULL.  Neither may overlap Q, K, V, the state or each other
  *            (Q8A_E_INVAL).
  * Everything else as for attn_accumulate_chunk. */
-int attn_accumulate_chunk_final(const q8a_state *st, const void *q, const void *k,
+int attn_accumulate_chunk_final(q8a_state *st, const void *q, const void *k,
                                 const void *v, int32_t kv_dtype, int64_t kv_pos0, int32_t n_kv,
                                 int64_t kv_head_stride, int64_t kv_seq_stride, int32_t causal,
                                 void *out, float *lse, void *stream);
@@ -157,7 +197,7 @@ int attn_accumulate_chunk_final(const q8a_state *st, const void *q, const void *
  *            written and the state is not.
  *   q, kv_pos0, n_kv, causal, stream: as for attn_accumulate_chunk.
  * Two launches on the stream (one pack of both tensors, one accumulate). */
-int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
+int attn_append_chunk(q8a_state *st, const void *q, const float *k_new,
                       const float *v_new, void *k_cache, void *v_cache, int64_t kv_pos0,
                       int32_t n_kv, int64_t kv_head_stride, int64_t kv_seq_stride,
                       int32_t causal, void *stream);
@@ -167,8 +207,8 @@ int attn_append_chunk(const q8a_state *st, const void *q, const float *k_new,
  * even; before that rounding within 1.5 FP32 ulps of O / l), and lse = m + ln(l) in FP32
  * (natural log).  Empty rows give out = 0 and
  * lse = -inf.  out: FP16 [n_seq][n_heads][n_q][64], 16-byte aligned; lse: FP32 [..][n_q] or NULL.
- * The state is not modified. */
-int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream);
+ * The state is not modified (a Q8A_STATE_FRESH state is first initialised, every row empty). */
+int attn_finalize(q8a_state *st, void *out, float *lse, void *stream);
 
 /* Merge the partial state src into dst.  Each must hold, for the same rows, the accumulation of
  * a key set, the two key sets disjoint; afterwards dst holds what accumulating both key sets
@@ -180,10 +220,12 @@ int attn_finalize(const q8a_state *st, void *out, float *lse, void *stream);
  * idle, as in Mode B of "Out-of-Core ...", Sec. 4) and merged afterwards; the same rule merges
  * states built on different devices.
  *   dst, src  initialised states with equal n_seq, n_heads, n_q and q_pos0 (else Q8A_E_STATE),
- *             whose buffers do not overlap (else Q8A_E_INVAL).  src is not modified.
+ *             whose buffers do not overlap (else Q8A_E_INVAL).  src is not modified.  A
+ *             Q8A_STATE_FRESH src holds no key: nothing is enqueued.  A Q8A_STATE_FRESH dst is
+ *             first initialised (every row empty).
  * Both states must be stream-ordered before the call (dst and src work on `stream` or
  * synchronised with it). */
-int attn_state_merge(const q8a_state *dst, const q8a_state *src, void *stream);
+int attn_state_merge(q8a_state *dst, const q8a_state *src, void *stream);
 
 /* Double-buffered streaming of a KV cache held in pinned host memory ("Out-of-Core ...", Sec. 2:
  * two ping-pong slots, chunk c+1 copied while chunk c is computed, handoff by synchronisation
@@ -194,7 +236,7 @@ int attn_state_merge(const q8a_state *dst, const q8a_state *src, void *stream);
  * chunk_bytes each, 16-byte aligned.  Copies run on copy_stream (hipMemcpyAsync host->device),
  * kernels on compute_stream; HIP events order slot reuse.  On return everything is enqueued;
  * compute_stream carries the completion of the last chunk.  Key positions start at 0. */
-int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_host,
+int attn_accumulate_stream(q8a_state *st, const void *q, const void *k_host,
                            const void *v_host, int32_t kv_dtype, int64_t n_kv_total,
                            int32_t chunk_tokens, void *const slot_k[2], void *const slot_v[2],
                            int32_t causal, void *compute_stream, void *copy_stream);
@@ -222,7 +264,7 @@ int attn_accumulate_stream(const q8a_state *st, const void *q, const void *k_hos
  * are no longer in use; compute_stream carries the completion of the last chunk.
  * Q8A_E_IO: a read failed or a file ended early; the chunks before it have been accumulated
  * (their work is enqueued), so the state then holds a prefix of the keys. */
-int attn_accumulate_file(const q8a_state *st, const void *q, int fd_k, int fd_v,
+int attn_accumulate_file(q8a_state *st, const void *q, int fd_k, int fd_v,
                          int64_t file_offset, int32_t kv_dtype, int64_t n_kv_total,
                          int32_t chunk_tokens, void *const ring_k[2], void *const ring_v[2],
                          int64_t ring_bytes, void *const slot_k[2], void *const slot_v[2],

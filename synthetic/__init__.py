@@ -159,6 +159,19 @@ def gen_kv_chunk(w: Workload, c: int, layer: int = 0):
             randn(shape, base + 101 + 2 * c))
 
 
+def gen_kv_chunk_head(w: Workload, c: int, h: int, layer: int = 0):
+    """Head h of gen_kv_chunk(w, c, layer): the same float32 K and V draws, [n_kv, 64] each, for
+    one head only."""
+    kv_pos0, n_kv = w.chunks()[c]
+    base = 1000 * w.wid + 100_000 * layer
+    out = []
+    for seed in (base + 100 + 2 * c, base + 101 + 2 * c):
+        t = torch.empty((n_kv, w.D), dtype=torch.float32)
+        t.normal_(generator=_gen(seed * 1_000_003 + h))
+        out.append(t.numpy())
+    return out[0], out[1]
+
+
 def sample_rows(w: Workload, rows_per_head: int | None = None) -> np.ndarray:
     """Flat row ids (b*H + h)*M + i, sorted, for the rows the oracle checks."""
     r = rows_per_head if rows_per_head is not None else w.rows_per_head

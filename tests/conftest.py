@@ -20,9 +20,12 @@ def orc():
 
 
 @pytest.fixture(params=["128", "256", "256k"])
-def rows_per_workgroup(request, monkeypatch):
+def rows_per_workgroup(request):
     """Run with each tile form of the accumulate kernel forced for more than 64 query rows: 128
     rows per workgroup, 256 rows, and 256 rows with every tile's keys split over 8 wavefronts
-    (tests without this fixture run the library's own choice)."""
-    monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", request.param)
-    return request.param
+    (tests without this fixture run the library's own choice).  The form is set in the flags of
+    every state gpu_util.new_state describes."""
+    import gpu_util
+    gpu_util.TILE_FORM[0] = gpu_util.FORMS[request.param]
+    yield request.param
+    gpu_util.TILE_FORM[0] = gpu_util.FORMS["auto"]

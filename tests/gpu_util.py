@@ -18,6 +18,24 @@ REL_RMS = 1e-3
 LSE_REL = 1e-4
 D = 64
 
+# the accumulate kernel's tile form, set in the flags of every state new_state describes (the
+# rows_per_workgroup fixture runs a test under each forced form)
+FORMS = {"auto": q8a.FORM_AUTO, "128": q8a.FORM_NARROW, "256": q8a.FORM_WIDE,
+         "256k": q8a.FORM_KEY_SPLIT}
+TILE_FORM = [q8a.FORM_AUTO]
+
+
+def new_state(B, H, M, q_pos0, deferred=False, flags=0):
+    """Allocate and describe a state (attn_state_init, or attn_state_init_deferred), with the
+    current TILE_FORM and any further flags set.  Returns (st, (m, l, o))."""
+    m, l, o = q8a.alloc_state(B, H, M)
+    if deferred:
+        st = q8a.attn_state_init_deferred(m, l, o, B, H, M, D, q_pos0)
+    else:
+        st = q8a.attn_state_init(m, l, o, B, H, M, D, q_pos0)
+    q8a.set_flags(st, TILE_FORM[0] | flags)
+    return st, (m, l, o)
+
 
 def say(*a):
     print(*a, flush=True)
@@ -47,8 +65,7 @@ def prefill(q, k, v, kv_dtype, B, H, M, N, q_pos0, chunks, causal=1, on_state=No
     (m, l, o)) as device tensors (out and lse None without the finalize)."""
     row = q8a.ROW_BYTES[kv_dtype]
     if state is None:
-        m, l, o = q8a.alloc_state(B, H, M)
-        st = q8a.attn_state_init(m, l, o, B, H, M, D, q_pos0)
+        st, (m, l, o) = new_state(B, H, M, q_pos0)
     else:
         st, (m, l, o) = state
     kp, vp = k.data_ptr(), v.data_ptr()

@@ -306,3 +306,69 @@ def test_binding_refuses_views_with_gaps():
         q8a.q8_0_pack(x, cache[:, :6], 12, 64)
     with pytest.raises(ValueError):
         q8a.q8_0_pack(x.transpose(0, 1), cache, 12, 64)
+
+
+def test_deferred_init_enqueues_nothing_and_checks_like_init():
+    """attn_state_init_deferred takes attn_state_init's checks and fills the descriptor with
+    Q8A_STATE_FRESH without touching the device: it succeeds on a host without a GPU."""
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    st = q8a.q8a_state()
+    ok = (P(A16), P(A16B), P(A16C))
+    assert lib.attn_state_init_deferred(ctypes.byref(st), *ok, 1, 4, 256, 128, 0) == \
+        q8a.Q8A_E_UNSUPPORTED
+    assert lib.attn_state_init_deferred(ctypes.byref(st), *ok, 0, 4, 256, 64, 0) == \
+        q8a.Q8A_E_INVAL
+    assert lib.attn_state_init_deferred(ctypes.byref(st), P(A16), P(A16B), P(A16C + 8), 1, 4,
+                                        256, 64, 0) == q8a.Q8A_E_ALIGN
+    assert lib.attn_state_init_deferred(ctypes.byref(st), *ok, 1, 1, 1 << 24, 64, 0) == \
+        q8a.Q8A_E_UNSUPPORTED
+    assert st.magic == 0
+    assert lib.attn_state_init_deferred(ctypes.byref(st), *ok, 2, 4, 256, 64, 7) == q8a.Q8A_OK
+    assert st.magic == q8a.STATE_MAGIC and st.flags == q8a.STATE_FRESH
+    assert (st.m, st.l, st.o, st.n_seq, st.n_heads, st.n_q, st.q_pos0) == \
+        (A16, A16B, A16C, 2, 4, 256, 7)
+
+
+def test_unknown_state_flags_are_rejected():
+    st = fake_state()
+    st.flags = 0x100
+    assert acc(st) == q8a.Q8A_E_STATE
+    assert q8a.library().attn_finalize(ctypes.byref(st), ctypes.c_void_p(A16), None, None) == \
+        q8a.Q8A_E_STATE
+
+
+@pytest.mark.skipif(not NO_GPU, reason="needs a host without a GPU")
+def test_fresh_bit_survives_a_failed_launch():
+    """A call on a FRESH state clears the bit only once its work is enqueued: with no device
+    the launch fails (Q8A_E_HIP) and the bit stays set, for every entry point that reads the
+    state; a FRESH src merges as a no-op."""
+    lib = q8a.library()
+    P = ctypes.c_void_p
+    for first_pos in (0, 300):  # every row sees the chunk / the initialisation comes first
+        st = separate_state()
+        st.flags = q8a.STATE_FRESH | q8a.FORM_NARROW
+        assert acc(st, pos=first_pos) == q8a.Q8A_E_HIP
+        assert st.flags == q8a.STATE_FRESH | q8a.FORM_NARROW
+        assert acc_final(st, pos=first_pos) == q8a.Q8A_E_HIP
+        assert st.flags & q8a.STATE_FRESH
+    st = fake_state()
+    st.flags = q8a.STATE_FRESH
+    assert lib.attn_finalize(ctypes.byref(st), P(0x9000000), None, None) == q8a.Q8A_E_HIP
+    assert st.flags == q8a.STATE_FRESH
+    a = fake_state()
+    b = fake_state()
+    b.m, b.l, b.o = 0x110000, 0x120000, 0x200000
+    b.flags = q8a.STATE_FRESH
+    assert lib.attn_state_merge(ctypes.byref(a), ctypes.byref(b), None) == q8a.Q8A_OK
+    a.flags = q8a.STATE_FRESH
+    b.flags = 0
+    assert lib.attn_state_merge(ctypes.byref(a), ctypes.byref(b), None) == q8a.Q8A_E_HIP
+    assert a.flags == q8a.STATE_FRESH
+
+
+def test_sub_state_of_a_deferred_state_is_refused():
+    st = fake_state(B=2)
+    st.flags = q8a.STATE_FRESH
+    with pytest.raises(ValueError):
+        q8a.sub_state(st, 1, 1)

@@ -48,24 +48,28 @@ def test_chunk_flops_brute_force():
         assert bench.chunk_flops(w, p0, n) == pairs * w.B * w.H * 4 * w.D
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_algorithmic_bytes_row_by_row(fused):
+@pytest.mark.parametrize("form", ["plain", "fused", "lean"])
+def test_algorithmic_bytes_row_by_row(form):
     """Per head and chunk: K and V rows (68 B each), and for every query row that sees a key of
-    the chunk its FP16 Q row (128 B), its state read (m always, 4 B; l and O, 260 B, unless the
-    row has seen no key before) and written (264 B); fused, also out (128 B) and lse (4 B) of the
-    rows whose position lies in the chunk."""
+    the chunk its FP16 Q row (128 B), its state read (m, 4 B, except in the lean form's first
+    call; l and O, 260 B, unless the row has seen no key before) and written (264 B, except the
+    lean form's completed rows); fused and lean, also out (128 B) and lse (4 B) of the rows
+    whose position lies in the chunk."""
     w = synthetic.Workload(99, "t", 2, 3, 40, 40, 0, 16, None)
-    got = bench.algorithmic_bytes(w, w.chunk, fused=fused)
+    got = bench.algorithmic_bytes(w, w.chunk, form=form)
     for c, (p0, n) in enumerate(w.chunks()):
         per_head = 2 * 68 * n
         for i in range(w.M):
             pos = w.q_pos0 + i
             if pos < p0:
                 continue
-            seen_before = pos >= 0 and p0 > 0
-            per_head += 128 + 4 + (260 if seen_before else 0) + 264
-            if fused and pos < p0 + n:
-                per_head += 128 + 4
+            seen_before = p0 > 0
+            completed = form != "plain" and pos < p0 + n
+            per_head += 128
+            per_head += 0 if (form == "lean" and p0 == 0) else 4
+            per_head += 260 if seen_before else 0
+            per_head += 0 if (form == "lean" and completed) else 264
+            per_head += 128 + 4 if completed else 0
         assert got[c] == per_head * w.B * w.H
 
 

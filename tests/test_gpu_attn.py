@@ -71,18 +71,22 @@ def test_small_cases(orc, case, rows_per_workgroup):
 
 @pytest.mark.parametrize("case", [(1, 2, 200, 200, 0, 64), (2, 3, 300, 520, 220, 100),
                                   (1, 4, 520, 520, 0, 520), (2, 2, 130, 333, 203, 100)])
-def test_row_forms_agree_bit_for_bit(orc, case, monkeypatch):
+def test_row_forms_agree_bit_for_bit(orc, case):
     """128- and 256-row workgroups compute every row the same way: the same state and output
     bits."""
+    import gpu_util
     B, H, M, N, q_pos0, bc = case
     n_alloc = (N + 3) // 4 * 4
     prob, qd, kd, vd = setup_case(orc, B, H, M, n_alloc, q_pos0, seed=sum(case))
     res = {}
     for rows in ("128", "256"):
-        monkeypatch.setenv("Q8A_ROWS_PER_WORKGROUP", rows)
         say("case", case, "rows per workgroup", rows)
-        out, lse, (m, l, o) = prefill(qd, kd, vd, q8a.KV_Q8_0, B, H, M, n_alloc, q_pos0,
-                                      chunk_list(N, bc))
+        gpu_util.TILE_FORM[0] = gpu_util.FORMS[rows]
+        try:
+            out, lse, (m, l, o) = prefill(qd, kd, vd, q8a.KV_Q8_0, B, H, M, n_alloc, q_pos0,
+                                          chunk_list(N, bc))
+        finally:
+            gpu_util.TILE_FORM[0] = gpu_util.FORMS["auto"]
         mm = m.cpu().numpy().reshape(-1)
         ne = ~np.isneginf(mm)
         res[rows] = (out.cpu().numpy().view(np.uint16), lse.cpu().numpy().view(np.uint32),

@@ -1,0 +1,213 @@
+"""GPU parity on inputs that reach the accumulate kernel's rarely taken branches, against the
+FP64 oracle element by element at the stated tolerances (max-abs 2e-3, rel-RMS 1e-3, LSE 1e-4
+relative with a floor of 1).
+
+* The rescale of the recurrence ("Out-of-Core Flash Streaming & Speculative Decode (1M
+  Context)", Sec. 3, steps 3-4: alpha = e^(m_old - m_new) << 1, exponent underflow).  The kernel
+  keeps a per-row reference maximum and moves it only when a 64-key tile's maximum exceeds it by
+  more than 8 log2 units, rescaling O and l by exp2(-delta) on that tile; N(0, 1) inputs almost
+  never do that.  Two constructions force it:
+    - Q scaled by 40: logits of about +-100, so the running maximum of most rows jumps by more
+      than 8 log2 units after their first tile and the weights of most keys underflow to 0.
+      V is drawn N(0, 0.5^2) there: such rows are dominated by one key, so |O| approaches the
+      largest |V| of the head; above 4 the FP16 output grid alone is 2^-8 apart (half-ulp
+      1.95e-3), and a test with |O| in [4, 8) would measure the output format rather than the
+      kernel.
+    - a ramp: dimension 0 of every query is 8 and of key j is 0.1 j, so every row's logits rise
+      by 0.1 per key (9.2 log2 units per tile): the reference moves on every tile and the
+      earliest keys' weights underflow FP32.
+  Each test first checks on the CPU, from the dequantised logits, that the case really moves a
+  finite reference by more than 8 log2 units (the kernel's tiles start at each chunk's first
+  key), and that exponent underflow occurs.
+* Degenerate block_q8_0 blocks ("Core Architecture & The 4-Brick Pipeline", Sec. 5): an all-zero
+  K (the oracle's closed form O = mean of the visible V, LSE = ln(p + 1)), keys whose second or
+  first block has scale 0 over nonzero int8 values (a valid block from another quantiser), and
+  subnormal FP16 scales in K and V.
+
+Every case runs under each tile form (128, 256 and 256 rows with key-split wavefronts), the at
+most 64-row split-key form and FP16 KV, in ascending and shuffled chunk order."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_flashattention_q8_amd as q8a
+import synthetic
+from gpu_util import D, assert_close, f16_to_dev, prefill, say
+from test_gpu_attn import chunk_list
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+KT = 64      # keys per tile of the accumulate kernel
+TAU = 8.0    # log2 units the tile maximum must exceed the reference by to move it
+
+
+def to_dev_bytes(b):
+    return torch.from_numpy(np.ascontiguousarray(b)).to("cuda")
+
+
+def logits_log2(orc, q, kb, N, q_pos0, causal, kv_dtype):
+    """Scaled logits in log2 units, float64 [rows, N] per (sequence, head) flattened; masked
+    entries -inf."""
+    if kv_dtype == q8a.KV_Q8_0:
+        K = orc.q8_0_dequant(kb)
+    else:
+        K = orc.f16_to_f64(kb)
+    K = K.reshape(-1, N, D)
+    Q = q.view(np.float16).astype(np.float64).reshape(K.shape[0], -1, D)
+    S = np.einsum("hmd,hnd->hmn", Q, K) / 8.0 * LOG2E
+    if causal:
+        pos = q_pos0 + np.arange(Q.shape[1])
+        S[:, np.arange(N)[None, :] > pos[:, None]] = -np.inf
+    return S.reshape(-1, N)
+
+
+def reference_moves(S2, calls):
+    """Rows whose reference maximum is raised from a finite value by more than TAU on some tile,
+    following the kernel's rule (tiles of KT keys from each call's first key; a call starts from
+    the running maximum of the keys before it), and the number of visible (row, key) pairs whose
+    weight exp2(s - max) underflows FP32 (s - max < -126)."""
+    moved = np.zeros(S2.shape[0], dtype=bool)
+    m_state = np.full(S2.shape[0], -np.inf)
+    for kv0, n in calls:
+        ref = m_state.copy()
+        for t0 in range(kv0, kv0 + n, KT):
+            blk = S2[:, t0:min(t0 + KT, kv0 + n)]
+            mx = blk.max(axis=1)
+            jump = np.isfinite(ref) & (mx > ref + TAU)
+            moved |= jump
+            ref = np.where(~np.isfinite(ref) | jump, np.maximum(ref, mx), ref)
+        m_state = np.maximum(m_state, S2[:, kv0:kv0 + n].max(axis=1))
+    top = S2.max(axis=1, keepdims=True)
+    under = int((np.isfinite(S2) & (S2 - top < -126)).sum())
+    return moved, under
+
+
+def run(orc, q, k, v, B, H, M, N, q_pos0, calls, causal=1, kv_dtype=q8a.KV_Q8_0, raw=None):
+    """HIP path (init, the calls in the given order, finalize) against the oracle; k, v float32
+    [B,H,N,64] (packed or rounded here), or raw = (kb, vb) bytes / FP16 bits as given."""
+    qd = f16_to_dev(q)
+    if raw is not None:
+        kb, vb = raw
+    elif kv_dtype == q8a.KV_Q8_0:
+        kb, vb = orc.q8_0_pack(k), orc.q8_0_pack(v)
+    else:
+        kb, vb = synthetic.to_f16_bits(k), synthetic.to_f16_bits(v)
+    if kv_dtype == q8a.KV_Q8_0:
+        kd, vd = to_dev_bytes(kb), to_dev_bytes(vb)
+    else:
+        kd, vd = f16_to_dev(kb), f16_to_dev(vb)
+    out, lse, _ = prefill(qd, kd, vd, kv_dtype, B, H, M, N, q_pos0, calls, causal)
+    prob = orc.Problem(q, kb, vb, orc.KV_Q8_0 if kv_dtype == q8a.KV_Q8_0 else orc.KV_F16,
+                       q_pos0)
+    prob.causal = bool(causal)
+    O_ref, lse_ref = orc.attention(prob)
+    return (out.float().cpu().numpy().reshape(-1, D), lse.cpu().numpy().reshape(-1), O_ref,
+            lse_ref, kb)
+
+
+# B, H, M, N, q_pos0, chunk, kv dtype: causal prefills whose rows see 321..1100 keys, split
+# into calls; M = 50 takes the split-key form
+STRESS = [
+    (1, 2, 200, 520, 320, 128, q8a.KV_Q8_0),
+    (2, 1, 300, 1100, 800, 256, q8a.KV_Q8_0),
+    (1, 2, 50, 1100, 1050, 200, q8a.KV_Q8_0),
+    (1, 2, 200, 520, 320, 128, q8a.KV_F16),
+]
+
+
+def stress_inputs(kind, B, H, M, N, q_pos0, seed):
+    q, k, v = synthetic.small_case(B, H, M, N, q_pos0, seed)
+    qf = q.view(np.float16).astype(np.float32)
+    if kind == "x40":
+        qf = qf * 40.0
+        v = v * 0.5
+    else:  # ramp
+        qf[..., 0] = 8.0
+        k[..., 0] = 0.1 * np.arange(N, dtype=np.float32)
+    return synthetic.to_f16_bits(qf), k, v
+
+
+@pytest.mark.parametrize("order", ["ascending", "shuffled"])
+@pytest.mark.parametrize("kind", ["x40", "ramp"])
+@pytest.mark.parametrize("case", STRESS, ids=[str(c) for c in STRESS])
+def test_rescale_branch(orc, case, kind, order, rows_per_workgroup):
+    B, H, M, N, q_pos0, bc, kv = case
+    say("rescale", kind, order, case, "rows per workgroup", rows_per_workgroup)
+    q, k, v = stress_inputs(kind, B, H, M, N, q_pos0, seed=sum(case[:6]))
+    calls = chunk_list(N, bc)
+    if order == "shuffled":
+        calls = [calls[i] for i in np.random.default_rng(5).permutation(len(calls))]
+    out, lse, O_ref, lse_ref, kb = run(orc, q, k, v, B, H, M, N, q_pos0, calls, kv_dtype=kv)
+    S2 = logits_log2(orc, q, kb, N, q_pos0, True, kv)
+    moved, under = reference_moves(S2, calls)
+    say("rows whose finite reference moves: %d of %d; underflowing pairs: %d"
+        % (moved.sum(), moved.size, under))
+    assert moved.sum() >= moved.size // 2
+    assert under > 0
+    assert_close(out, lse, O_ref, lse_ref, "%s %s %s" % (kind, order, case))
+
+
+@pytest.mark.parametrize("case", [(1, 2, 200, 260, 0, 64), (2, 1, 300, 520, 220, 100),
+                                  (1, 2, 40, 300, 260, 64)])
+def test_zero_keys(orc, case, rows_per_workgroup):
+    """K = 0 (every block all-zero: scale 0, int8 0): all logits 0, so every visible key weighs
+    the same; the oracle's closed form is O = mean of the visible V and LSE = ln(p + 1)."""
+    B, H, M, N, q_pos0, bc = case
+    say("zero keys", case, "rows per workgroup", rows_per_workgroup)
+    q, k, v = synthetic.small_case(B, H, M, N, q_pos0, seed=sum(case))
+    k[:] = 0.0
+    out, lse, O_ref, lse_ref, kb = run(orc, q, k, v, B, H, M, N, q_pos0, chunk_list(N, bc))
+    assert not kb.any()
+    pos = np.tile(q_pos0 + np.arange(M), B * H)
+    np.testing.assert_allclose(lse_ref, np.log(np.minimum(pos, N - 1) + 1.0), rtol=1e-12)
+    assert_close(out, lse, O_ref, lse_ref, "zero keys " + str(case))
+
+
+def degenerate_rows(orc, k, seed):
+    """Q8_0 bytes of k with per-key defects written into the block headers: scale 0 over the
+    nonzero int8 values of block 1, of block 0, of both, subnormal FP16 scales in either block,
+    and all-zero rows; about a third of the keys keep their packed bytes."""
+    kb = orc.q8_0_pack(k).copy()
+    rows = kb.reshape(-1, 68)
+    rng = np.random.default_rng(seed)
+    kind = rng.integers(0, 9, size=rows.shape[0])
+    sub = rng.integers(1, 1024, size=(rows.shape[0], 2)).astype(np.uint16)  # subnormal bits
+    for r in range(rows.shape[0]):
+        kd = kind[r]
+        if kd == 0:
+            rows[r, 34:36] = 0                      # d1 = 0, q1 != 0
+        elif kd == 1:
+            rows[r, 0:2] = 0                        # d0 = 0, q0 != 0
+        elif kd == 2:
+            rows[r, 0:2] = 0                        # both scales 0
+            rows[r, 34:36] = 0
+        elif kd == 3:
+            rows[r, 0:2] = sub[r, 0:1].view(np.uint8)    # subnormal d0
+        elif kd == 4:
+            rows[r, 34:36] = sub[r, 1:2].view(np.uint8)  # subnormal d1
+        elif kd == 5:
+            rows[r, :] = 0                          # all-zero row
+    return kb
+
+
+# B, H, M, N (keys in the cache), keys the chunks cover, q_pos0, chunk, causal.  Chunks of 33 or
+# 333 keys end off a 16-byte boundary (the masked unpack); the causal rows never see the keys
+# past the last chunk.
+DEGENERATE = [(1, 2, 200, 400, 400, 200, 100, 1), (2, 1, 130, 336, 333, 203, 33, 1),
+              (1, 2, 48, 256, 256, 0, 96, 0)]
+
+
+@pytest.mark.parametrize("case", DEGENERATE, ids=[str(c) for c in DEGENERATE])
+def test_degenerate_blocks(orc, case, rows_per_workgroup):
+    """Keys and values whose blocks carry zero or subnormal scales (see degenerate_rows), causal
+    and not; the oracle decodes every value as q * d16, so a zero scale zeroes its block."""
+    B, H, M, N, n_cover, q_pos0, bc, causal = case
+    say("degenerate blocks", case, "rows per workgroup", rows_per_workgroup)
+    q, k, v = synthetic.small_case(B, H, M, N, q_pos0, seed=sum(case))
+    kb = degenerate_rows(orc, k, seed=1)
+    vb = degenerate_rows(orc, v, seed=2)
+    assert not causal or q_pos0 + M <= n_cover
+    out, lse, O_ref, lse_ref, _ = run(orc, q, None, None, B, H, M, N, q_pos0,
+                                      chunk_list(n_cover, bc), causal=causal, raw=(kb, vb))
+    assert_close(out, lse, O_ref, lse_ref, "degenerate " + str(case))
