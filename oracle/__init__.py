@@ -30,6 +30,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q8_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libq8oracle.so")
+# the sanitizer tier (tests/test_sanitizers.py) points this at an instrumented build of the
+# same source
+_LIB_OVERRIDE = os.environ.get("Q8_ORACLE_LIB")
 _lib = None
 
 KV_Q8_0 = 0
@@ -60,9 +63,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     lib.orc_f16_to_f64.restype = ctypes.c_double

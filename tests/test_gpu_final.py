@@ -203,7 +203,7 @@ def test_fresh_finalize_and_merge(orc):
     assert not out.any() and torch.all(torch.isneginf(lse))
 
     src, (mf, lf, of) = new_state(B, H, M, q_pos0)
-    prefill(qd, kd, vd, Q8, B, H, M, N, q_pos0, chunk_list(N, 50), state=(src, (mf, lf, of)),
+    prefill(qd, kd, vd, Q8, B, H, M, N, q_pos0, chunk_list(N, 48), state=(src, (mf, lf, of)),
             finalize=False)
     fresh, (m2, l2, o2) = new_state(B, H, M, q_pos0, deferred=True)
     before = [t.clone() for t in (mf, lf, of)]

@@ -13,9 +13,10 @@ relative with a floor of 1).
       largest |V| of the head; above 4 the FP16 output grid alone is 2^-8 apart (half-ulp
       1.95e-3), and a test with |O| in [4, 8) would measure the output format rather than the
       kernel.
-    - a ramp: dimension 0 of every query is 8 and of key j is 0.1 j, so every row's logits rise
-      by 0.1 per key (9.2 log2 units per tile): the reference moves on every tile and the
-      earliest keys' weights underflow FP32.
+    - a ramp: dimension 0 of every query is 8 and of key j is 0.25 j, so every row's logits rise
+      by 0.25 per key (23 log2 units per tile, far above the other dimensions' noise): the
+      reference moves on every tile, and a row that sees 520 keys spans about 190 log2 units,
+      so the earliest keys' weights underflow FP32.
   Each test first checks on the CPU, from the dequantised logits, that the case really moves a
   finite reference by more than 8 log2 units (the kernel's tiles start at each chunk's first
   key), and that exponent underflow occurs.
@@ -124,7 +125,7 @@ def stress_inputs(kind, B, H, M, N, q_pos0, seed):
         v = v * 0.5
     else:  # ramp
         qf[..., 0] = 8.0
-        k[..., 0] = 0.1 * np.arange(N, dtype=np.float32)
+        k[..., 0] = 0.25 * np.arange(N, dtype=np.float32)
     return synthetic.to_f16_bits(qf), k, v
 
 
@@ -191,10 +192,10 @@ def degenerate_rows(orc, k, seed):
     return kb
 
 
-# B, H, M, N (keys in the cache), keys the chunks cover, q_pos0, chunk, causal.  Chunks of 33 or
-# 333 keys end off a 16-byte boundary (the masked unpack); the causal rows never see the keys
-# past the last chunk.
-DEGENERATE = [(1, 2, 200, 400, 400, 200, 100, 1), (2, 1, 130, 336, 333, 203, 33, 1),
+# B, H, M, N (keys in the cache), keys the chunks cover, q_pos0, chunk, causal.  Chunks start on
+# 16-byte boundaries (multiples of 4 keys); the last chunk of 33 keys ends off one (the masked
+# unpack), and the causal rows never see the keys past it.
+DEGENERATE = [(1, 2, 200, 400, 400, 200, 100, 1), (2, 1, 130, 336, 333, 203, 100, 1),
               (1, 2, 48, 256, 256, 0, 96, 0)]
 
 
