@@ -218,12 +218,17 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             // second block's products are added unscaled (S0 * kr + S1), so its int8 values are
             // taken as 0 here; the first block needs nothing, its products are multiplied by
             // kr = d0 / d1 = 0 (or by d0 = 0 when both scales are 0).
-            const uint32_t zk = (blk == 1 && d1 == 0.f) ? 0u : 0xFFFFFFFFu;
             uint32_t w[4];
-            w[0] = __builtin_amdgcn_alignbyte(x1, x0, sh) & zk;
-            w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh) & zk;
-            w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh) & zk;
-            w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh) & zk;
+            w[0] = __builtin_amdgcn_alignbyte(x1, x0, sh);
+            w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh);
+            w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh);
+            w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh);
+            const bool zero1 = blk == 1 && d1 == 0.f;
+            if (__builtin_amdgcn_ballot_w64(zero1)) { // rare: a block scale of 0
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = zero1 ? 0u : w[i];
+            }
             half8 q8[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -278,3 +278,31 @@ def test_workload_append_133k(orc):
     """The 131,072 cached tokens through attn_accumulate_chunk, the 2048 appended tokens (the
     queries' own positions) through attn_append_chunk from FP32."""
     run_workload(orc, 3, append=True)
+
+
+# Chunks of 512 keys and more: in the 256-row form the state's O of resumed rows reaches the
+# kernel spread over its first tiles (8 KiB blocks of 32 rows through LDS); exactly 8 tiles (the
+# last block is added after the loop) and more than 8; ragged query tiles; states whose rows are
+# partly empty (a chunk after some query positions first); chunk orders that resume rows from a
+# later chunk.
+BIG_CHUNKS = [
+    # B, H, M, N, q_pos0, chunk, order of the chunks (indices into the ascending list)
+    (1, 2, 300, 1600, 1300, 512, None),         # 8-tile calls, the last call one tile
+    (2, 1, 260, 2000, 1740, 640, None),         # 10-tile calls
+    (1, 2, 600, 1024, 0, 512, (1, 0)),          # rows 512..599 resumed, rows 0..511 fresh
+    (1, 1, 256, 1536, 1024, 512, (2, 0, 1)),    # the diagonal chunk first
+]
+
+
+@pytest.mark.parametrize("case", BIG_CHUNKS, ids=[str(c) for c in BIG_CHUNKS])
+def test_big_chunks(orc, case, rows_per_workgroup):
+    B, H, M, N, q_pos0, bc, order = case
+    say("big chunks", case, "rows per workgroup", rows_per_workgroup)
+    prob, qd, kd, vd = setup_case(orc, B, H, M, N, q_pos0, seed=sum(case[:6]))
+    chunks = chunk_list(N, bc)
+    if order is not None:
+        chunks = [chunks[i] for i in order]
+    out, lse, _ = prefill(qd, kd, vd, q8a.KV_Q8_0, B, H, M, N, q_pos0, chunks)
+    O_ref, lse_ref = orc.attention(prob)
+    assert_close(out.float().cpu().numpy().reshape(-1, D), lse.cpu().numpy().reshape(-1),
+                 O_ref, lse_ref, str(case))
