@@ -127,6 +127,21 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, half2v &lo, half2v &hi)
     hi = biased_pair_to_f16(u, 0x04030402u);
 }
 
+// The same for K values that are kept only when `keep` is 1 and become 0 when it is 0 (the
+// products with a block whose scale is 0): (u - 1152) * keep as one fused multiply-add
+// u * keep - 1152 * keep, exact for keep = 1, and +0 for keep = 0 (u is finite).
+__device__ __forceinline__ void i8x4_to_f16_keep(uint32_t w, half2v keep, half2v nbias,
+                                                 half2v &lo, half2v &hi)
+{
+    const uint32_t u = w ^ 0x80808080u;
+    lo = __builtin_elementwise_fma(
+        __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kF16Magic, u, 0x04010400u)), keep,
+        nbias);
+    hi = __builtin_elementwise_fma(
+        __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kF16Magic, u, 0x04030402u)), keep,
+        nbias);
+}
+
 // Position of key r (0..63) inside the transposed V tile and the V-scale vector: bits 2 and 3
 // swapped, so that the 8 keys one lane contributes to a PV step are contiguous.
 __device__ __forceinline__ int vpos(int r)
@@ -216,24 +231,34 @@ __device__ __forceinline__ void unpack_tile(const uint8_t *__restrict__ rk,
             const float d1 = (float)*reinterpret_cast<const _Float16 *>(rr + 34);
             // A block whose scale is 0 contributes 0 whatever its int8 values (q * 0).  The
             // second block's products are added unscaled (S0 * kr + S1), so its int8 values are
-            // taken as 0 here; the first block needs nothing, its products are multiplied by
-            // kr = d0 / d1 = 0 (or by d0 = 0 when both scales are 0).
+            // taken as 0 here (in the conversion itself, at no extra instruction); the first
+            // block needs nothing, its products are multiplied by kr = d0 / d1 = 0 (or by d0 = 0
+            // when both scales are 0).
             uint32_t w[4];
             w[0] = __builtin_amdgcn_alignbyte(x1, x0, sh);
             w[1] = __builtin_amdgcn_alignbyte(x2, x1, sh);
             w[2] = __builtin_amdgcn_alignbyte(x3, x2, sh);
             w[3] = __builtin_amdgcn_alignbyte(x4, x3, sh);
             const bool zero1 = blk == 1 && d1 == 0.f;
-            if (__builtin_amdgcn_ballot_w64(zero1)) { // rare: a block scale of 0
+            const _Float16 kp = zero1 ? (_Float16)0.0f : (_Float16)1.0f;
+            const _Float16 nb = zero1 ? (_Float16)0.0f : (_Float16)-1152.0f;
+            const half2v keep = {kp, kp}, nbias = {nb, nb};
+            if constexpr (MASK) {
+                // (the masked form has no registers to spare for the two factors: a branch)
+                if (__builtin_amdgcn_ballot_w64(zero1)) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = zero1 ? 0u : w[i];
+                    for (int i = 0; i < 4; ++i)
+                        w[i] = zero1 ? 0u : w[i];
+                }
             }
             half8 q8[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 half2v q01, q23;
-                i8x4_to_f16(w[i], q01, q23);
+                if constexpr (MASK)
+                    i8x4_to_f16(w[i], q01, q23);
+                else
+                    i8x4_to_f16_keep(w[i], keep, nbias, q01, q23);
                 q8[i >> 1][4 * (i & 1) + 0] = q01[0]; q8[i >> 1][4 * (i & 1) + 1] = q01[1];
                 q8[i >> 1][4 * (i & 1) + 2] = q23[0]; q8[i >> 1][4 * (i & 1) + 3] = q23[1];
             }
@@ -737,7 +762,7 @@ void accumulate_kernel(AccumulateArgs a)
                 // O^T += V^T P^T.  Block 0's products overlap block 1's exponentials.
 #pragma unroll
                 for (int j = JLO; j < NJ; ++j) {
-                    float ls[4] = {0.f, 0.f, 0.f, 0.f}; // four partial sums: shorter chains
+                    float ls[4]; // four partial sums: shorter chains
                     half8 p16[NS][2];
 #pragma unroll
                     for (int si = 0; si < NS; ++si) {
@@ -745,7 +770,9 @@ void accumulate_kernel(AccumulateArgs a)
                         for (int v = 0; v < 16; ++v) {
                             const float p = __builtin_amdgcn_exp2f(s[j][si][v]);
                             s[j][si][v] = p;
-                            ls[v & 3] += p;
+                            // the first four start the sums (not 0 + p: the compiler may not
+                            // drop that addition, which would turn -0 into +0)
+                            ls[v & 3] = (si == 0 && v < 4) ? p : ls[v & 3] + p;
                         }
                         p16[si][0] = to_half8(s[j][si], 0);
                         p16[si][1] = to_half8(s[j][si], 8);
@@ -822,12 +849,14 @@ void accumulate_kernel(AccumulateArgs a)
             const float mn = fmaxf(ma, mb);
             const float fa = (ma == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ma - mn);
             const float fb = __builtin_amdgcn_exp2f(mb - mn);
+            // one product, then one fused multiply-add, written out so that every instantiation
+            // rounds the merge of the two key halves the same way
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                o[j][0][v] = o[j][0][v] * fa + xb[v] * fb;
-                o[j][1][v] = o[j][1][v] * fa + xb[16 + v] * fb;
+                o[j][0][v] = __builtin_fmaf(xb[v], fb, o[j][0][v] * fa);
+                o[j][1][v] = __builtin_fmaf(xb[16 + v], fb, o[j][1][v] * fa);
             }
-            l_part[j] = l_part[j] * fa + xb[32] * fb;
+            l_part[j] = __builtin_fmaf(xb[32], fb, l_part[j] * fa);
             m_ref[j] = mn;
         }
         m_top[j] = fmaxf(m_top[j], xb[34]);
