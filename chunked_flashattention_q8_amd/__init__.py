@@ -35,11 +35,12 @@ STATE_MAGIC = 0x51384154
 # bits of q8a_state.flags (include/q8attn.h)
 STATE_FRESH = 0x1
 STATE_FINAL_OUT_ONLY = 0x2
-FORM_MASK = 0x30
+FORM_MASK = 0x70
 FORM_AUTO = 0x00
 FORM_WIDE = 0x10
 FORM_NARROW = 0x20
 FORM_KEY_SPLIT = 0x30
+FORM_SPLIT = 0x40
 HEAD_DIM = 64
 ROW_BYTES = {KV_Q8_0: 68, KV_F16: 128}
 

@@ -34,7 +34,8 @@ int row_bytes(int32_t kv_dtype)
 
 int check_state(const q8a_state *st)
 {
-    if (!st || st->magic != Q8A_STATE_MAGIC || (st->flags & ~Q8A_STATE_FLAGS_KNOWN))
+    if (!st || st->magic != Q8A_STATE_MAGIC || (st->flags & ~Q8A_STATE_FLAGS_KNOWN) ||
+        (st->flags & Q8A_FORM_MASK) > Q8A_FORM_SPLIT)
         return Q8A_E_STATE;
     if (st->head_dim != q8a::kHeadDim || st->n_seq < 1 || st->n_heads < 1 || st->n_q < 1 ||
         !st->m || !st->l || !st->o || st->q_pos0 < 0)
@@ -106,6 +107,7 @@ q8a::AccumulateArgs make_args(const q8a_state *st, const void *q, const void *k,
     case Q8A_FORM_WIDE: a.form = q8a::kFormWide; break;
     case Q8A_FORM_NARROW: a.form = q8a::kFormNarrow; break;
     case Q8A_FORM_KEY_SPLIT: a.form = q8a::kFormKeySplit; break;
+    case Q8A_FORM_SPLIT: a.form = q8a::kFormSplit; break;
     default: a.form = q8a::kFormAuto;
     }
     return a;

@@ -367,7 +367,7 @@ void accumulate_kernel(AccumulateArgs a)
     constexpr bool KSPLIT = SPLIT || KS8;        // wavefronts split every tile's keys
     constexpr int NJ = (SPLIT || NARROW) ? 1 : 2; // 32-row query blocks per wavefront
     constexpr int NS = KSPLIT ? 1 : 2;            // 32-key subtiles per wavefront and tile
-    constexpr int QTF = NARROW ? QT / 2 : QT;     // query rows per workgroup
+    constexpr int QTF = SPLIT ? 2 * WQ : NARROW ? QT / 2 : QT; // query rows per workgroup
     constexpr int ROW = Smem<FMT>::ROW;
     constexpr int RAW16 = KT * ROW / 16;                 // 16-byte pieces per tensor tile
     constexpr int NPRE = KS8 ? 2 : FMT == 0 ? 3 : 4;     // prefetch slots per thread
@@ -1117,7 +1117,7 @@ static int workgroup_slots()
 template <int FMT, bool CLEAN>
 static void launch_form(const AccumulateArgs &a, int form, hipStream_t s)
 {
-    const int rows = form == kNarrow ? QT / 2 : QT;
+    const int rows = form == kSplit ? 2 * WQ : form == kNarrow ? QT / 2 : QT;
     const int64_t n_qt = (a.M + rows - 1) / rows;
     int64_t first_row = 0;
     if (a.causal && a.kv_pos0 > a.q_pos0)
@@ -1144,17 +1144,27 @@ static void launch_form(const AccumulateArgs &a, int form, hipStream_t s)
 hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t s)
 {
     // The tile form.  Up to 64 query rows (two blocks): split the keys of every tile between
-    // wavefront pairs.  Otherwise 256-row workgroups, unless they would not fill the chip's
+    // wavefront pairs.  Otherwise 256-row workgroups, unless the launch would not fill the chip's
     // workgroup slots (2 per compute unit):
     //   * where the causal diagonal crosses the chunk so that the first row sees less than half
     //     of what the last row sees, the query tiles' work is uneven and the launch lasts as
-    //     long as the tile that sees the most; 128-row workgroups halve that tile's work per key;
+    //     long as the tile that sees the most; 128-row workgroups halve that tile's work per key,
+    //     and where even 64-row workgroups would fill at most half the slots (the last chunk of
+    //     a short causal prefill, which only the diagonal rows see), those with key-split
+    //     wavefront pairs quarter it;
     //   * otherwise the load is (nearly) even; with at most one workgroup per compute unit, the
     //     8-wavefront key-split form gives every SIMD two wavefronts while each K/V tile is
     //     still unpacked once for 256 rows.
+    // Workgroup counts are those launched: the query tiles that hold a row seeing the chunk.
     // a.form, when set, fixes the form for more than 64 rows.
     const int slots = workgroup_slots();
-    const int64_t wide = (int64_t)((a.M + QT - 1) / QT) * a.B * a.H;
+    int64_t first_row = 0;
+    if (a.causal && a.kv_pos0 > a.q_pos0)
+        first_row = std::min<int64_t>(a.kv_pos0 - a.q_pos0, a.M);
+    auto launched = [&](int rows) {
+        return (int64_t)((a.M + rows - 1) / rows - first_row / rows) * a.B * a.H;
+    };
+    const int64_t wide = launched(QT);
     // keys of the chunk the first and the last query row see (at least one for the first)
     auto clamp_keys = [&](int64_t n, int64_t lo) {
         return std::min<int64_t>(std::max(n, lo), a.n_kv);
@@ -1165,15 +1175,21 @@ hipError_t launch_accumulate(const AccumulateArgs &a, int kv_dtype, hipStream_t 
     int form = kWide;
     if (a.M <= 2 * WQ)
         form = kSplit;
-    else if (wide < slots)
-        form = uneven ? kNarrow : 2 * wide <= slots ? kKeySplit : kWide;
-    if (form != kSplit) {
+    else if (wide < slots) {
+        if (uneven)
+            form = 2 * launched(2 * WQ) <= slots ? kSplit : kNarrow;
+        else
+            form = 2 * wide <= slots ? kKeySplit : kWide;
+    }
+    if (a.M > 2 * WQ) {
         if (a.form == kFormNarrow)
             form = kNarrow;
         else if (a.form == kFormWide)
             form = kWide;
         else if (a.form == kFormKeySplit)
             form = kKeySplit;
+        else if (a.form == kFormSplit)
+            form = kSplit;
     }
     if (kv_dtype != 0)
         launch_form<1, true>(a, form, s); // FP16 rows: 128 bytes, always clean

@@ -38,7 +38,7 @@ struct AccumulateArgs {
 };
 
 // forced tile forms of the accumulate kernel (AccumulateArgs::form)
-constexpr int kFormAuto = 0, kFormWide = 1, kFormNarrow = 2, kFormKeySplit = 3;
+constexpr int kFormAuto = 0, kFormWide = 1, kFormNarrow = 2, kFormKeySplit = 3, kFormSplit = 4;
 
 hipError_t launch_q8_0_pack(const float *x, uint8_t *dst, int64_t n_blocks, hipStream_t s);
 // K and V rows [n_seq][n_heads][n_rows][64] FP32 -> Q8_0 rows at k_dst / v_dst + b * seq_stride

@@ -89,15 +89,16 @@ typedef struct {
  *   completed rows' state must not be finalised, merged or accumulated further.
  * Q8A_FORM_*: the accumulate kernel's tile form for states of more than 64 query rows, for
  *   tuning and tests (Q8A_FORM_AUTO, 0, lets the library choose; see attn_accumulate_chunk).
- *   WIDE and NARROW give the same results bit for bit; KEY_SPLIT sums in another order and agrees
- *   with them to rounding. */
+ *   WIDE and NARROW give the same results bit for bit; KEY_SPLIT and SPLIT sum in other orders
+ *   and agree with them to rounding.  Values above Q8A_FORM_SPLIT are reserved (Q8A_E_STATE). */
 #define Q8A_STATE_FRESH 0x1u
 #define Q8A_STATE_FINAL_OUT_ONLY 0x2u
-#define Q8A_FORM_MASK 0x30u
+#define Q8A_FORM_MASK 0x70u
 #define Q8A_FORM_AUTO 0x00u      /* the library's choice */
 #define Q8A_FORM_WIDE 0x10u      /* 256 query rows per workgroup, 4 wavefronts */
 #define Q8A_FORM_NARROW 0x20u    /* 128 query rows per workgroup, 4 wavefronts */
 #define Q8A_FORM_KEY_SPLIT 0x30u /* 256 query rows, 8 wavefronts splitting each tile's keys */
+#define Q8A_FORM_SPLIT 0x40u     /* 64 query rows, 4 wavefronts splitting each tile's keys */
 #define Q8A_STATE_FLAGS_KNOWN (Q8A_STATE_FRESH | Q8A_STATE_FINAL_OUT_ONLY | Q8A_FORM_MASK)
 
 /* Q8_0 pack ("Core Architecture & The 4-Brick Pipeline", Sec. 5, block_q8_0; row size from

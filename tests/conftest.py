@@ -19,12 +19,13 @@ def orc():
     return oracle
 
 
-@pytest.fixture(params=["128", "256", "256k"])
+@pytest.fixture(params=["128", "256", "256k", "64"])
 def rows_per_workgroup(request):
     """Run with each tile form of the accumulate kernel forced for more than 64 query rows: 128
-    rows per workgroup, 256 rows, and 256 rows with every tile's keys split over 8 wavefronts
-    (tests without this fixture run the library's own choice).  The form is set in the flags of
-    every state gpu_util.new_state describes."""
+    rows per workgroup, 256 rows, 256 rows with every tile's keys split over 8 wavefronts, and
+    64 rows with every tile's keys split over wavefront pairs (tests without this fixture run
+    the library's own choice).  The form is set in the flags of every state
+    gpu_util.new_state describes."""
     import gpu_util
     gpu_util.TILE_FORM[0] = gpu_util.FORMS[request.param]
     yield request.param

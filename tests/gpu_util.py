@@ -21,7 +21,7 @@ D = 64
 # the accumulate kernel's tile form, set in the flags of every state new_state describes (the
 # rows_per_workgroup fixture runs a test under each forced form)
 FORMS = {"auto": q8a.FORM_AUTO, "128": q8a.FORM_NARROW, "256": q8a.FORM_WIDE,
-         "256k": q8a.FORM_KEY_SPLIT}
+         "256k": q8a.FORM_KEY_SPLIT, "64": q8a.FORM_SPLIT}
 TILE_FORM = [q8a.FORM_AUTO]
 
 

@@ -334,6 +334,9 @@ def test_unknown_state_flags_are_rejected():
     st = fake_state()
     st.flags = 0x100
     assert acc(st) == q8a.Q8A_E_STATE
+    for form in (0x50, 0x60, 0x70):  # reserved tile forms
+        st.flags = form
+        assert acc(st) == q8a.Q8A_E_STATE
     assert q8a.library().attn_finalize(ctypes.byref(st), ctypes.c_void_p(A16), None, None) == \
         q8a.Q8A_E_STATE
 
