@@ -84,3 +84,29 @@ def test_pack_destination_alignment_and_odd_block_counts(orc, n_rows, row_len, o
     got = buf.cpu().numpy()
     assert np.array_equal(got[offset:offset + n_bytes], orc.q8_0_pack(x).reshape(-1))
     assert (got[:offset] == 0xA5).all() and (got[offset + n_bytes:] == 0xA5).all()
+
+
+def test_pack_scales_across_the_fp16_range(orc):
+    """Block maxima from 1e-9 to 3e4 (FP16 scales that are zero, subnormal, normal and near the
+    largest finite value), a dense sweep of maxima around 127 * 2^-14 (where the FP16 scale turns
+    from subnormal to normal), then the same blocks with most values moved onto the
+    quantiser's ties of their own scale and 0, 1 or 2 ulps either side."""
+    rng = np.random.default_rng(11)
+    amax = np.exp(rng.uniform(np.log(1e-9), np.log(3e4), size=4096))
+    sweep = 127 * 2.0 ** -14 * (1 + np.linspace(-0.02, 0.02, 2048))
+    amax = np.concatenate([amax, sweep]).astype(np.float32)
+    x = (rng.uniform(-1, 1, size=(amax.size, 32)) * amax[:, None]).astype(np.float32)
+    x[:, 0] = amax
+    say("pack scale range", x.shape)
+    ref = orc.q8_0_pack(x.reshape(-1, 64))
+    assert np.array_equal(pack_rows(x.reshape(-1, 64), 64), ref)
+    d16 = ref.reshape(-1, 34)[:, :2].copy().view(np.float16).astype(np.float32).reshape(-1)
+    k = rng.integers(-126, 126, size=(amax.size, 31)) + 0.5
+    t = (k * d16[:, None]).astype(np.float32)
+    for _ in range(2):
+        step = rng.integers(-1, 2, size=t.shape)
+        t = np.where(step > 0, np.nextafter(t, np.float32(np.inf)),
+                     np.where(step < 0, np.nextafter(t, np.float32(-np.inf)), t)).astype(np.float32)
+    x[:, 1:] = t
+    say("pack scale range, ties", x.shape)
+    assert np.array_equal(pack_rows(x.reshape(-1, 64), 64), orc.q8_0_pack(x.reshape(-1, 64)))
