@@ -896,11 +896,11 @@ void accumulate_kernel(AccumulateArgs a)
     // out and lse are written as the finalize kernel would from the state just stored (the same
     // FP32 values, the same reciprocal, product and logarithm), flag 2 instead of 1.
     constexpr int kStagePitch = 68;                                // floats per staged row
-    constexpr int kStageFloats = WQ * kStagePitch + 2 * WQ;        // rows, flags, final l
+    constexpr int kStageFloats = WQ * kStagePitch + 2 * WQ;        // rows, flags, final 1/l
     constexpr int kStageBase = 2 * 64 * 36;                        // floats
     static_assert(sizeof(Smem<FMT>) >= 4 * (kStageBase + 4 * kStageFloats), "staging area");
     float *stg = reinterpret_cast<float *>(&sm) + kStageBase + wave * kStageFloats;
-    float *stg_flag = stg + WQ * kStagePitch, *stg_l = stg_flag + WQ;
+    float *stg_flag = stg + WQ * kStagePitch, *stg_l = stg_flag + WQ; // flags, final rows' 1/l
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (kv_end_b[j] > 0 && (!KSPLIT || kh == 0)) { // uniform per wavefront
@@ -932,7 +932,9 @@ void accumulate_kernel(AccumulateArgs a)
             // output alone
             if (g == 0) {
                 stg_flag[qcol] = wr ? (fin ? (a.final_out_only ? 3.f : 2.f) : 1.f) : 0.f;
-                stg_l[qcol] = l_st;
+                // the final rows' reciprocal of l, formed once by the lane that owns the row
+                if (fin_block)
+                    stg_l[qcol] = final_inv_l(l_st);
             }
             const uint32_t ml_off = (st_ml && g == 0) ? (q0 + qcol) * 4u : kNoRow;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_st), rs_m, ml_off, 0,
@@ -966,7 +968,7 @@ void accumulate_kernel(AccumulateArgs a)
 #pragma unroll
                 for (int i = 0; i < WQ / 4; ++i) {
                     const int r = 4 * i + (lane >> 4), c = lane & 15;
-                    const float rl = final_inv_l(stg_l[r]);
+                    const float rl = stg_l[r];
                     const uint32_t oo =
                         stg_flag[r] >= 2.f ? (q0 + r) * (kHeadDim * 2u) + 8u * c : kNoRow;
                     const half4 h = {final_out(__uint_as_float(vv[i][0]), rl),
