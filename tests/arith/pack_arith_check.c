@@ -10,8 +10,9 @@
  *    |d| < 1/2 - 2^-13, r equals round(RN(x / dh)) with halves away from zero, clamped to
  *    [-127, 127], and the low byte of f's bits is r as a two's-complement byte.  Checked for
  *    every normal FP16 scale, three reciprocals (RN(1/dh) and one FP32 ulp either side), and for
- *    each integer k in [-127, 127] the inputs x within 3 ulps of k * dh and of (k + 1/2) * dh that
- *    the scale's block can hold (|x| <= 127 * dh * (1 + 2^-11)).
+ *    each integer k in [-127, 127] the inputs x within 3 ulps of k * dh, of (k + 1/2) * dh and of
+ *    the window's edges (k + 1/2 -+ 2^-13) * dh that the scale's block can hold
+ *    (|x| <= 127 * dh * (1 + 2^-11)).
  *
  * Prints "mismatches A B" (the counts of the two checks) and exits 0 when both are zero. */
 #include <math.h>
@@ -52,8 +53,11 @@ static void *run(void *p)
         const float rn = 1.0f / dh;
         const float rdhs[3] = {nextafterf(rn, 0.0f), rn, nextafterf(rn, INFINITY)};
         for (int k = -127; k <= 127; ++k) {
-            for (int half = 0; half < 2; ++half) {
-                const float c = ((float)k + (half ? 0.5f : 0.0f)) * dh; /* exact: <= 9 bits x 11 */
+            for (int half = 0; half < 4; ++half) {
+                /* k dh and (k + 1/2) dh (exact: at most 9 bits times 11), and the edges of the
+                 * window, (k + 1/2 -+ 2^-13) dh rounded to FP32 */
+                const double off[4] = {0.0, 0.5, 0.5 - 0x1p-13, 0.5 + 0x1p-13};
+                const float c = (float)(((double)k + off[half]) * (double)dh);
                 float x = c;
                 for (int i = 0; i < 3; ++i)
                     x = nextafterf(x, -INFINITY);
