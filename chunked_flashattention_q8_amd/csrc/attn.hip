@@ -896,11 +896,15 @@ void accumulate_kernel(AccumulateArgs a)
     // out and lse are written as the finalize kernel would from the state just stored (the same
     // FP32 values, the same reciprocal, product and logarithm), flag 2 instead of 1.
     constexpr int kStagePitch = 68;                                // floats per staged row
-    constexpr int kStageFloats = WQ * kStagePitch + 2 * WQ;        // rows, flags, final 1/l
+    constexpr int kStageFloats = WQ * kStagePitch + 3 * WQ;        // rows, 2 offsets, final 1/l
     constexpr int kStageBase = 2 * 64 * 36;                        // floats
     static_assert(sizeof(Smem<FMT>) >= 4 * (kStageBase + 4 * kStageFloats), "staging area");
     float *stg = reinterpret_cast<float *>(&sm) + kStageBase + wave * kStageFloats;
-    float *stg_flag = stg + WQ * kStagePitch, *stg_l = stg_flag + WQ; // flags, final rows' 1/l
+    // per staged row: its byte offset in the state's O and in out (past the range where the row
+    // is not written), and a final row's 1/l
+    uint32_t *stg_off = reinterpret_cast<uint32_t *>(stg + WQ * kStagePitch);
+    uint32_t *stg_oo = stg_off + WQ;
+    float *stg_l = reinterpret_cast<float *>(stg_oo + WQ);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         if (kv_end_b[j] > 0 && (!KSPLIT || kh == 0)) { // uniform per wavefront
@@ -928,10 +932,13 @@ void accumulate_kernel(AccumulateArgs a)
             // are dropped
             const uint32_t q0 = (uint32_t)block_q0(j);
             const float m_st = m_top[j] * kLn2, l_st = l_tot * rr; // the stored m and l
-            // row flags: 0 nothing, 1 the state, 2 the state and the final output, 3 the final
-            // output alone
+            // the lane that owns a row stages where its state row and its output row go: the
+            // state of a row that saw a key unless it is final and its state dead, the output of
+            // a final row
             if (g == 0) {
-                stg_flag[qcol] = wr ? (fin ? (a.final_out_only ? 3.f : 2.f) : 1.f) : 0.f;
+                const uint32_t rq = q0 + (uint32_t)qcol;
+                stg_off[qcol] = (wr && !(fin && a.final_out_only)) ? rq * (kHeadDim * 4u) : kNoRow;
+                stg_oo[qcol] = (wr && fin) ? rq * (kHeadDim * 2u) : kNoRow;
                 // the final rows' reciprocal of l, formed once by the lane that owns the row
                 if (fin_block)
                     stg_l[qcol] = final_inv_l(l_st);
@@ -947,15 +954,14 @@ void accumulate_kernel(AccumulateArgs a)
                     make_rsrc(a.lse + head * a.M, (uint32_t)a.M * 4u),
                     (fin && g == 0) ? (q0 + qcol) * 4u : kNoRow, 0, kStoreThrough);
             // the same wavefront reads back what it wrote (LDS keeps a wavefront's order): all
-            // rows and flags first, so the LDS reads overlap, then the stores
+            // rows and offsets first, so the LDS reads overlap, then the stores
             u32x4 vv[WQ / 4];
             uint32_t off[WQ / 4];
 #pragma unroll
             for (int i = 0; i < WQ / 4; ++i) {
                 const int r = 4 * i + (lane >> 4), c = lane & 15;
                 vv[i] = *reinterpret_cast<const u32x4 *>(&stg[r * kStagePitch + 4 * c]);
-                const float fl = stg_flag[r];
-                off[i] = (fl == 1.f || fl == 2.f) ? (q0 + r) * (kHeadDim * 4u) + 16u * c : kNoRow;
+                off[i] = stg_off[r] + 16u * c; // past the range stays past it: kNoRow + 240
             }
 #pragma unroll
             for (int i = 0; i < WQ / 4; ++i)
@@ -969,8 +975,7 @@ void accumulate_kernel(AccumulateArgs a)
                 for (int i = 0; i < WQ / 4; ++i) {
                     const int r = 4 * i + (lane >> 4), c = lane & 15;
                     const float rl = stg_l[r];
-                    const uint32_t oo =
-                        stg_flag[r] >= 2.f ? (q0 + r) * (kHeadDim * 2u) + 8u * c : kNoRow;
+                    const uint32_t oo = stg_oo[r] + 8u * c;
                     const half4 h = {final_out(__uint_as_float(vv[i][0]), rl),
                                      final_out(__uint_as_float(vv[i][1]), rl),
                                      final_out(__uint_as_float(vv[i][2]), rl),
