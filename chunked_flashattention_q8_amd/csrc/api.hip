@@ -40,6 +40,12 @@ int check_state(const q8a_state *st)
     if (st->head_dim != q8a::kHeadDim || st->n_seq < 1 || st->n_heads < 1 || st->n_q < 1 ||
         !st->m || !st->l || !st->o || st->q_pos0 < 0)
         return Q8A_E_STATE;
+    // sizes attn_state_init refuses as unsupported (a descriptor edited by hand): the launch
+    // geometry relies on them
+    if (st->n_heads > 65535 || st->n_seq > 65535 || st->n_q > kMaxRows ||
+        (int64_t)st->n_seq * st->n_heads > ((int64_t)1 << 23) ||
+        (int64_t)st->n_seq * st->n_heads * st->n_q > ((int64_t)1 << 28))
+        return Q8A_E_UNSUPPORTED;
     return Q8A_OK;
 }
 

@@ -330,6 +330,16 @@ def test_deferred_init_enqueues_nothing_and_checks_like_init():
         (A16, A16B, A16C, 2, 4, 256, 7)
 
 
+def test_hand_edited_descriptor_sizes_are_rejected():
+    """A descriptor with sizes attn_state_init refuses as unsupported (edited by hand after
+    init) is refused the same way by every call that reads it, before anything is enqueued."""
+    for B, H, M in ((65535, 200, 1), (4096, 4096, 1), (1, 64, (1 << 23) + 1), (1, 1, 1 << 24)):
+        st = fake_state(B=B, H=H, M=M)
+        assert acc(st, ss=256 * 68 * H) == q8a.Q8A_E_UNSUPPORTED, (B, H, M)
+        assert q8a.library().attn_finalize(ctypes.byref(st), ctypes.c_void_p(A16), None,
+                                           None) == q8a.Q8A_E_UNSUPPORTED, (B, H, M)
+
+
 def test_unknown_state_flags_are_rejected():
     st = fake_state()
     st.flags = 0x100
