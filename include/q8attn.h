@@ -60,7 +60,10 @@ typedef enum {
  * A descriptor of sequences [s0, s0 + n) of an initialised state is a copy of its descriptor
  * with m and l advanced by s0*n_heads*n_q floats, o by 64 times that, and n_seq = n; it may be
  * passed wherever a state is (for example to merge sequence blocks of one state).  Take such
- * copies only of a descriptor without Q8A_STATE_FRESH (each copy would initialise on its own). */
+ * copies only of a descriptor without Q8A_STATE_FRESH (each copy would initialise on its own).
+ * Every call that reads a descriptor checks it as attn_state_init checks its arguments: a
+ * descriptor edited to sizes that call refuses gives Q8A_E_UNSUPPORTED, one without the magic,
+ * with head_dim other than 64 or with unknown flag bits Q8A_E_STATE. */
 typedef struct {
     float *m;          /* [n_seq][n_heads][n_q]      running maximum of the scaled logits  */
     float *l;          /* [n_seq][n_heads][n_q]      running sum of e^(S - m)             */
