@@ -746,11 +746,16 @@ void accumulate_kernel(AccumulateArgs a)
 #pragma unroll
                     for (int j = JLO; j < NJ; ++j) {
                         const float delta = need[j] ? mx[j] : 0.f; // new ref = base + delta
-                        const float alpha = (m_ref[j] == -INFINITY)
-                                                ? 0.f : __builtin_amdgcn_exp2f(-delta);
-                        l_part[j] *= alpha;
-                        o[j][0] *= alpha;
-                        o[j][1] *= alpha;
+                        // rows whose reference is still -inf hold l = 0 and O = 0: only rows
+                        // with a finite reference that moves need their sums rescaled (the first
+                        // tile of a fresh state has none)
+                        if (__builtin_amdgcn_ballot_w64(need[j] && m_ref[j] != -INFINITY)) {
+                            const float alpha = (m_ref[j] == -INFINITY)
+                                                    ? 0.f : __builtin_amdgcn_exp2f(-delta);
+                            l_part[j] *= alpha;
+                            o[j][0] *= alpha;
+                            o[j][1] *= alpha;
+                        }
                         if (need[j])
                             m_ref[j] = base[j] + delta;
 #pragma unroll
